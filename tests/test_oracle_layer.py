@@ -1,0 +1,209 @@
+"""Pins for the oracle's experts and combine (the layer output).
+
+Expert math from "DeepSeek-V3.2-Exp / Mixture of experts / Shared expert" ("All 5 steps" and the MLP
+forward excerpt); combine from the MoE forward excerpt on the same page.  The checks here do not reuse the
+oracle's formulae: they use torch's linear algebra on special cases that reduce the layer to one dense
+SwiGLU, closed forms with permutation matrices, the page's printed parameter counts, exact power-of-two
+homogeneity and token-permutation equivariance.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from sparse_mixture_experts_08_amd import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+F32, BF16, FP8 = W.F32, W.BF16, W.FP8_E4M3
+
+
+def _np(inp, *names):
+    return [W.to_numpy(inp.get(n)) for n in names]
+
+
+def _run_oracle(oracle, wl, inp, tokens=None):
+    x, Wg, bias = _np(inp, "x", "Wg", "bias")
+    r = oracle.route(x, Wg, bias, wl.k, wl.act_dtype)
+    ws = _np(inp, "W1", "W3", "W2", "S1", "S3", "S2")
+    sc = dict(zip(["W1s", "W3s", "W2s", "S1s", "S3s", "S2s"], _np(inp, "W1s", "W3s", "W2s", "S1s", "S3s", "S2s")))
+    out, y = oracle.forward(wl.shape(), x, *ws, r["idx"], r["w"], tokens=tokens, **sc)
+    return r, out, y
+
+
+def _y_float(wl, y):
+    return torch.from_numpy(y.astype(np.float32)) if wl.act_dtype == F32 else \
+        torch.from_numpy(y.view(np.int16).copy()).view(torch.bfloat16).float()
+
+
+def test_parameter_count_matches_page_table():
+    g = json.load(open(os.path.join(HERE, "golden", "param_count.json")))
+    wl = W.DECODE_BF16
+    assert (wl.d, wl.inter) == (g["d"], g["inter"])
+    shapes = W.weight_shapes(wl)
+    n1 = math.prod(shapes["W1"][1:])
+    n3 = math.prod(shapes["W3"][1:])
+    n2 = math.prod(shapes["W2"][1:])
+    assert (n1, n3, n2) == (g["gate_projection"], g["up_projection"], g["down_projection"])
+    assert n1 + n3 + n2 == g["per_instance_total"]
+    assert sum(math.prod(shapes[s]) for s in ("S1", "S3", "S2")) == g["per_instance_total"]
+    assert g["per_instance_total"] * g["moe_blocks"] == g["across_moe_blocks"]
+
+
+def test_spec_table_shapes():
+    g = json.load(open(os.path.join(HERE, "golden", "spec_table.json")))
+    for wl in W.CONFIGS[1:]:
+        assert (wl.E, wl.k) == (g["routed_experts"], g["activated_routed_experts"])
+        assert wl.inter_shared == g["shared_experts"] * wl.inter
+    assert g["layers"] - g["dense_layers"] == json.load(open(os.path.join(HERE, "golden", "param_count.json")))["moe_blocks"]
+
+
+def _torch_act_quant(v):
+    """Independent 1x128 activation quantiser built from torch's float8 conversion."""
+    R, C = v.shape
+    g = v.float().view(R, C // 128, 128)
+    amax = g.abs().amax(-1, keepdim=True)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (g / s).to(torch.float8_e4m3fn).float()
+    return (q.double() * s.double()).view(R, C)
+
+
+def _torch_dequant_w(q, s):
+    R, C = q.shape
+    qf = q.view(torch.float8_e4m3fn).double()
+    return qf * s.double().repeat_interleave(128, 0).repeat_interleave(128, 1)
+
+
+def _torch_swiglu(wl, x, w1, w3, w2, s1=None, s3=None, s2=None):
+    """Dense SwiGLU w2(silu(w1 x) * w3 x) in torch with the layer's rounding points."""
+    rnd = (lambda t: t.float()) if wl.act_dtype == F32 else (lambda t: t.float().to(torch.bfloat16).float())
+    if wl.w_dtype == FP8:
+        xin, W1d, W3d, W2d = _torch_act_quant(x), _torch_dequant_w(w1, s1), _torch_dequant_w(w3, s3), _torch_dequant_w(w2, s2)
+    else:
+        xin, W1d, W3d, W2d = x.double(), w1.double(), w3.double(), w2.double()
+    g = rnd(xin @ W1d.T)
+    u = rnd(xin @ W3d.T)
+    h = rnd(F.silu(g) * u)
+    hin = _torch_act_quant(h) if wl.w_dtype == FP8 else h.double()
+    return rnd(hin @ W2d.T)
+
+
+@pytest.mark.parametrize("wl", [
+    W.Workload("dense-red-f32", 37, 256, 8, 3, 384, 128, F32, F32),
+    W.Workload("dense-red-bf16", 37, 256, 8, 3, 384, 128, BF16, BF16),
+    W.Workload("dense-red-fp8", 29, 384, 8, 3, 256, 128, BF16, FP8),
+], ids=lambda w: w.name)
+def test_dense_swiglu_reduction(oracle, wl):
+    # A +1e4 logit bias on expert e* sends every token there with weights (1, 0, ...) exactly; with the
+    # shared expert's W2 zeroed the layer is the single dense SwiGLU of the page's MLP formula.
+    inp = W.generate(wl, seed=11, device="cpu")
+    e_star = 5
+    bias = torch.zeros(wl.E)
+    bias[e_star] = 1e4
+    inp["bias"] = bias
+    inp["S2"] = torch.zeros_like(inp["S2"])
+    r, out, y = _run_oracle(oracle, wl, inp)
+    assert (r["idx"][:, 0] == e_star).all() and (r["w"][:, 0] == 1.0).all() and (r["w"][:, 1:] == 0).all()
+    assert r["counts"][e_star] == wl.T
+    sc = [inp.get(n) for n in ("W1s", "W3s", "W2s")]
+    sc = [None if s is None else s[e_star] for s in sc]
+    ref = _torch_swiglu(wl, inp["x"], inp["W1"][e_star], inp["W3"][e_star], inp["W2"][e_star], *sc)
+    got = _y_float(wl, y)
+    rel = float((got.double() - ref.double()).norm() / ref.double().norm())
+    same = float((got == ref).float().mean())
+    if wl.act_dtype == F32:          # fp32 silu differs by ulps between libm and torch
+        assert rel <= 1e-6, rel
+    else:                            # bf16 rounding absorbs them: most elements agree bitwise
+        assert rel <= 2e-3 and same >= 0.95, (rel, same)
+
+
+def test_permutation_matrix_closed_form(oracle):
+    # W1, W3, W2 permutation matrices: g_n = x[pi(n)], u_n = x[sigma(n)], y_m = h[rho(m)]
+    n = 64
+    wl = W.Workload("perm", 16, n, 4, 1, n, n, F32, F32)
+    inp = W.generate(wl, seed=12, device="cpu")
+    g = torch.Generator().manual_seed(12)
+    pi, sigma, rho = (torch.randperm(n, generator=g) for _ in range(3))
+    eye = torch.eye(n)
+    for e in range(wl.E):
+        inp["W1"][e], inp["W3"][e], inp["W2"][e] = eye[pi], eye[sigma], eye[rho]
+    inp["S2"] = torch.zeros_like(inp["S2"])
+    r, out, y = _run_oracle(oracle, wl, inp)
+    x = inp["x"].numpy()
+    gg, uu = x[:, pi.numpy()], x[:, sigma.numpy()]
+    h = (gg * (np.float32(1) / (np.float32(1) + np.exp(-gg)))) * uu
+    expected = h[:, rho.numpy()] * r["w"][:, :1]       # k = 1: weight is exactly 1
+    assert np.allclose(y, expected, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("wl", [
+    W.Workload("homog-bf16", 23, 256, 8, 3, 256, 128, BF16, BF16),
+    W.Workload("homog-fp8", 19, 256, 8, 3, 256, 128, BF16, FP8),
+], ids=lambda w: w.name)
+def test_power_of_two_homogeneity(oracle, wl):
+    # Doubling every W3 (routed and shared) doubles u, h and y exactly; so does doubling every W2.
+    inp = W.generate(wl, seed=13, device="cpu")
+    _, _, y0 = _run_oracle(oracle, wl, inp)
+    y0f = _y_float(wl, y0)
+    for names in (("W3", "S3"), ("W2", "S2")):
+        mod = dict(inp)
+        for nme in names:
+            if wl.w_dtype == FP8:
+                mod[nme + "s"] = inp[nme + "s"] * 2
+            else:
+                mod[nme] = inp[nme] * 2
+        _, _, y1 = _run_oracle(oracle, wl, mod)
+        assert torch.equal(_y_float(wl, y1), 2 * y0f), names
+
+
+def test_forward_token_permutation_equivariance_and_sampling(oracle):
+    wl = W.Workload("equiv-bf16", 40, 256, 16, 4, 128, 128, BF16, BF16)
+    inp = W.generate(wl, seed=14, device="cpu")
+    r, out, y = _run_oracle(oracle, wl, inp)
+    perm = torch.randperm(wl.T, generator=torch.Generator().manual_seed(14))
+    mod = dict(inp)
+    mod["x"] = inp["x"][perm]
+    _, out_p, y_p = _run_oracle(oracle, wl, mod)
+    assert np.array_equal(y_p, y[perm.numpy()]) and np.array_equal(out_p, out[perm.numpy()])
+    # a token sample gives the same rows as the full run
+    toks = np.array([39, 0, 17, 17, 5], np.int32)
+    _, out_s, y_s = _run_oracle(oracle, wl, inp, tokens=toks)
+    assert np.array_equal(y_s, y[toks]) and np.array_equal(out_s, out[toks])
+
+
+def test_zero_input_gives_zero_output(oracle):
+    wl = W.Workload("zero", 8, 128, 8, 2, 128, 128, BF16, BF16)
+    inp = W.generate(wl, seed=15, device="cpu")
+    inp["x"] = torch.zeros_like(inp["x"])
+    r, out, y = _run_oracle(oracle, wl, inp)
+    assert (out == 0).all() and (y == 0).all()
+
+
+def test_shared_expert_only_when_routed_w2_zero(oracle):
+    wl = W.Workload("shared-only", 21, 256, 8, 3, 128, 256, BF16, BF16)
+    inp = W.generate(wl, seed=16, device="cpu")
+    inp["W2"] = torch.zeros_like(inp["W2"])
+    r, out, y = _run_oracle(oracle, wl, inp)
+    ref = _torch_swiglu(wl, inp["x"], inp["S1"], inp["S3"], inp["S2"])
+    got = _y_float(wl, y)
+    rel = float((got.double() - ref.double()).norm() / ref.double().norm())
+    assert rel <= 2e-3, rel
+
+
+def test_combine_is_weighted_sum_of_experts_plus_shared(oracle):
+    # y = sum_j w_j SwiGLU_{idx_j}(x) + SwiGLU_shared(x), each expert output taken from the dense
+    # reduction above (torch); checked in fp64 against the oracle's fp32 accumulator.
+    wl = W.Workload("combine-f32", 24, 128, 6, 3, 128, 64, F32, F32)
+    inp = W.generate(wl, seed=17, device="cpu")
+    r, out, y = _run_oracle(oracle, wl, inp)
+    ref = _torch_swiglu(wl, inp["x"], inp["S1"], inp["S3"], inp["S2"]).double()
+    for t in range(wl.T):
+        for j in range(wl.k):
+            e = int(r["idx"][t, j])
+            ye = _torch_swiglu(wl, inp["x"][t:t + 1], inp["W1"][e], inp["W3"][e], inp["W2"][e]).double()
+            ref[t] += float(r["w"][t, j]) * ye[0]
+    rel = float((torch.from_numpy(out).double() - ref).norm() / ref.norm())
+    assert rel <= 1e-5, rel

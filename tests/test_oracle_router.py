@@ -1,0 +1,192 @@
+"""Pins for the oracle's router (logits, top-k, softmax) and routing artefacts.
+
+Gate as stated on "DeepSeek-V3's mixture-of-experts architecture explained", block pseudocode:
+logits = gate(x); top-8 of the logits; softmax over the selected values.  Artefacts as the MoE forward
+excerpt on "DeepSeek-V3.2-Exp / Mixture of experts" computes them: bincount of the indices and
+torch.where(indices == i) per expert.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_mixture_experts_08_amd import workloads as W
+
+F32, BF16 = 0, 1
+
+
+def _bf16(t):
+    return W.to_numpy(t.to(torch.bfloat16))
+
+
+def test_logits_one_hot_rows_pick_wg_rows(oracle):
+    # x = e_i  ->  logit[e] = Wg[i, e] exactly (catches a transposed or mis-indexed Wg)
+    d, E = 48, 20
+    g = torch.Generator().manual_seed(0)
+    Wg = torch.randn(d, E, generator=g)
+    x = torch.eye(d)
+    L = oracle.router_logits(x.numpy(), Wg.numpy(), None, F32)
+    assert np.array_equal(L, Wg.numpy())
+
+
+def test_logits_exact_on_small_integers(oracle):
+    # small integers: every FMA of the chain is exact, so the logits are the exact integer sums
+    T, d, E = 9, 300, 17
+    g = torch.Generator().manual_seed(1)
+    x = torch.randint(-8, 9, (T, d), generator=g).float()
+    Wg = torch.randint(-16, 17, (d, E), generator=g).float()
+    L = oracle.router_logits(_bf16(x), Wg.numpy(), None, BF16)
+    exact = x.long() @ Wg.long()
+    assert np.array_equal(L, exact.numpy().astype(np.float32))
+
+
+def test_logits_within_fp32_chain_error_bound(oracle):
+    # |fl(sum) - sum| <= gamma_d * sum |x_i w_i|, gamma_d = d u / (1 - d u), u = 2^-24, for any
+    # sequential fp32 FMA chain; the exact sum is formed with rationals.
+    T, d, E = 3, 257, 5
+    g = torch.Generator().manual_seed(2)
+    x = torch.randn(T, d, generator=g).to(torch.bfloat16)
+    Wg = torch.randn(d, E, generator=g)
+    L = oracle.router_logits(W.to_numpy(x), Wg.numpy(), None, BF16)
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    xf = x.float()
+    for t in range(T):
+        for e in range(E):
+            prods = [Fraction(float(xf[t, i])) * Fraction(float(Wg[i, e])) for i in range(d)]
+            exact = sum(prods)
+            bound = gamma * float(sum(abs(p) for p in prods))
+            assert abs(Fraction(float(L[t, e])) - exact) <= Fraction(bound)
+
+
+def test_logits_bias_is_one_fp32_add(oracle):
+    T, d, E = 11, 64, 16
+    g = torch.Generator().manual_seed(3)
+    x = _bf16(torch.randn(T, d, generator=g))
+    Wg = torch.randn(d, E, generator=g).numpy()
+    b = torch.randn(E, generator=g).numpy()
+    L0 = oracle.router_logits(x, Wg, None, BF16)
+    L1 = oracle.router_logits(x, Wg, b, BF16)
+    assert np.array_equal(L1, (L0 + b).astype(np.float32))
+
+
+def _ranks_above(L, a, b):
+    return L[a] > L[b] or (L[a] == L[b] and a < b)
+
+
+def test_topk_brute_force_over_subsets(oracle):
+    # With integer-valued logits, ties are frequent.  Exactly one k-subset has every member ranked
+    # above every non-member; idx must be that subset in rank order.
+    g = torch.Generator().manual_seed(4)
+    for E, k in [(6, 1), (7, 2), (8, 3), (10, 4), (9, 9)]:
+        T, d = 40, 3
+        x = torch.randint(-2, 3, (T, d), generator=g).float()
+        Wg = torch.randint(-1, 2, (d, E), generator=g).float()
+        r = oracle.route(_bf16(x), Wg.numpy(), None, k, BF16)
+        L = r["logits"]
+        for t in range(T):
+            winners = [S for S in itertools.combinations(range(E), k)
+                       if all(_ranks_above(L[t], a, b) for a in S for b in range(E) if b not in S)]
+            assert len(winners) == 1
+            order = sorted(winners[0], key=lambda e: (-L[t, e], e))
+            assert list(r["idx"][t]) == order
+
+
+def test_topk_equals_stable_sort_and_duplicate_columns_tie_low_first(oracle):
+    T, d, E, k = 64, 32, 24, 6
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(T, d, generator=g)
+    Wg = torch.randn(d, E, generator=g)
+    Wg[:, 13] = Wg[:, 4]          # duplicated columns: identical logits for experts 4 and 13
+    Wg[:, 20] = Wg[:, 19]
+    r = oracle.route(_bf16(x), Wg.numpy(), None, k, BF16)
+    L = torch.from_numpy(r["logits"])
+    assert torch.equal(L[:, 4], L[:, 13])
+    ref = torch.sort(-L, dim=1, stable=True).indices[:, :k]
+    assert torch.equal(torch.from_numpy(r["idx"]).long(), ref)
+    for t in range(T):
+        row = list(r["idx"][t])
+        if 13 in row:
+            assert 4 in row and row.index(4) < row.index(13)
+
+
+def test_zero_input_routes_to_lowest_indices_with_equal_weights(oracle):
+    T, d, E, k = 5, 64, 16, 4
+    x = np.zeros((T, d), np.float32)
+    Wg = torch.randn(d, E, generator=torch.Generator().manual_seed(6)).numpy()
+    r = oracle.route(x, Wg, None, k, F32)
+    assert (r["idx"] == np.arange(k)).all()
+    assert (r["w"] == np.float32(1.0 / k)).all()
+
+
+def test_softmax_closed_forms(oracle):
+    g = torch.Generator().manual_seed(7)
+    x = _bf16(torch.randn(50, 40, generator=g))
+    Wg = torch.randn(40, 12, generator=g).numpy()
+    r1 = oracle.route(x, Wg, None, 1, BF16)
+    assert (r1["w"] == 1.0).all()                                      # k = 1: weight exactly 1
+    r2 = oracle.route(x, Wg, None, 2, BF16)
+    L = r2["logits"].astype(np.float64)
+    l0 = np.take_along_axis(L, r2["idx"][:, :1].astype(np.int64), 1)[:, 0]
+    l1 = np.take_along_axis(L, r2["idx"][:, 1:2].astype(np.int64), 1)[:, 0]
+    w0 = 1.0 / (1.0 + np.exp(l1 - l0))                                 # k = 2: logistic of the gap
+    assert np.allclose(r2["w"][:, 0], w0, rtol=2 ** -23, atol=0)
+    assert np.allclose(r2["w"][:, 1], 1 - w0, rtol=2 ** -22, atol=1e-12)
+
+
+def test_routing_invariants_and_reference_calls(oracle):
+    T, d, E, k = 300, 96, 32, 5
+    g = torch.Generator().manual_seed(8)
+    x = _bf16(torch.randn(T, d, generator=g))
+    Wg = (torch.randn(d, E, generator=g) / math.sqrt(d)).numpy()
+    r = oracle.route(x, Wg, None, k, BF16)
+    idx = torch.from_numpy(r["idx"]).long()
+    w = r["w"]
+    # k distinct experts per token, weights positive, non-increasing, summing to 1 within rounding
+    assert all(len(set(row)) == k for row in r["idx"].tolist())
+    assert (w > 0).all() and (np.diff(w, axis=1) <= 0).all()
+    assert np.abs(w.astype(np.float64).sum(1) - 1).max() <= k * 2.0 ** -23
+    # bincount / torch.where, the reference code's own calls
+    counts = torch.bincount(idx.flatten(), minlength=E)
+    assert np.array_equal(r["counts"], counts.numpy()) and r["counts"].sum() == T * k
+    assert r["offsets"][0] == 0 and r["offsets"][E] == T * k
+    assert np.array_equal(np.diff(r["offsets"]), r["counts"])
+    expected = []
+    for e in range(E):
+        tt, jj = torch.where(idx == e)                # row-major: tokens ascending
+        expected += (tt * k + jj).tolist()
+    assert r["sorted_slots"].tolist() == expected
+    assert np.array_equal(r["sorted_slots"][r["pos"]], np.arange(T * k))
+
+
+def test_token_permutation_equivariance(oracle):
+    T, d, E, k = 64, 80, 16, 3
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn(T, d, generator=g)
+    Wg = torch.randn(d, E, generator=g).numpy()
+    perm = torch.randperm(T, generator=g)
+    r = oracle.route(_bf16(x), Wg, None, k, BF16)
+    rp = oracle.route(_bf16(x[perm]), Wg, None, k, BF16)
+    assert np.array_equal(rp["idx"], r["idx"][perm.numpy()])
+    assert np.array_equal(rp["w"], r["w"][perm.numpy()])
+
+
+def test_skewed_workload_routing_statistics(oracle):
+    # The skewed workload's bias concentrates tokens on the top-ranked experts and starves many others.
+    wl = W.SKEW_BF16.with_T(256)
+    inp = W.generate(wl, seed=0, device="cpu", weights=False)
+    r = oracle.route(W.to_numpy(inp["x"]), W.to_numpy(inp["Wg"]), W.to_numpy(inp["bias"]), wl.k, BF16)
+    c = np.sort(r["counts"])[::-1]
+    assert c[0] >= 0.9 * wl.T and c[1] >= 0.8 * wl.T                 # hottest experts see most tokens
+    assert (r["counts"] == 0).sum() >= 80                             # many experts receive nothing
+
+
+def test_uniform_workload_routing_statistics(oracle):
+    wl = W.PREFILL_BF16.with_T(512)
+    inp = W.generate(wl, seed=0, device="cpu", weights=False)
+    r = oracle.route(W.to_numpy(inp["x"]), W.to_numpy(inp["Wg"]), None, wl.k, BF16)
+    mean = wl.T * wl.k / wl.E
+    assert r["counts"].max() <= 3 * mean and (r["counts"] > 0).sum() >= 0.95 * wl.E
