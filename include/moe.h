@@ -1,0 +1,147 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of one DeepSeek-V3-style mixture-of-experts
+ * feed-forward layer.
+ *
+ * The layer (per token t, x[t] a row of d activations):
+ *   logits[e] = sum_i x[t][i] * Wg[i][e]  (+ bias[e])                       router, fp32
+ *   (idx, v)  = the k largest logits, descending, equal logits -> lower e
+ *   w         = softmax(v) over the k selected logits only
+ *   y[t]      = sum_j w[j] * SwiGLU_{idx[j]}(x[t]) + SwiGLU_shared(x[t])
+ *   SwiGLU(x) = W2 (silu(W1 x) * (W3 x))
+ * as stated on "DeepSeek-V3's mixture-of-experts architecture explained" (block pseudocode of
+ * "The architecture in one diagram": gate, topk, softmax over the selected values) and on
+ * "DeepSeek-V3.2-Exp / Mixture of experts / Shared expert" ("All 5 steps"; the MoE forward excerpt:
+ * fp32 accumulation of expert(x) * weight per expert, then + shared_experts(x); the MLP forward
+ * excerpt: silu * mul formed in fp32, cast back to the activation dtype before w2).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by the caller.  The
+ *    library allocates and frees nothing and keeps no state between calls.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream) without any host
+ *    synchronisation; results are valid once the caller synchronises the stream.
+ *  - Argument errors are detected on the host before any launch; nothing is written then.
+ *    Launch failures return MOE_ERR_HIP.  Device faults surface at the caller's next synchronisation.
+ *  - Calls are reentrant.  Concurrent calls must use different workspaces and outputs.
+ *  - Inputs are assumed finite; NaN/Inf inputs are outside the contract.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null required pointer, negative size, k > E, y aliasing x, bad alignment */
+    MOE_ERR_UNSUPPORTED = 2,   /* dtype combination, d / inter not multiples of 128, k > 16, E > 1024 */
+    MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 4            /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum {
+    MOE_F32 = 0,               /* IEEE binary32 */
+    MOE_BF16 = 1,              /* bfloat16 */
+    MOE_FP8_E4M3 = 2           /* OCP 8-bit E4M3 ("FN": max 448, no infinities), weights only */
+} moe_dtype_t;
+
+/*
+ * Sizes and dtypes of one layer invocation.
+ *   T             tokens (rows of x and y), T >= 0
+ *   d             model width (7168 for DeepSeek-V3), multiple of 128
+ *   E             routed experts (256), 1 <= E <= 1024
+ *   k             experts per token (8), 1 <= k <= min(E, 16)
+ *   inter         routed expert width (2048), multiple of 128
+ *   inter_shared  shared expert width (n_shared * inter = 2048), multiple of 128
+ *   act_dtype     dtype of x, y and every activation between linears: MOE_F32 or MOE_BF16
+ *   w_dtype       dtype of W1, W3, W2 and S1, S3, S2.  Supported pairs (act, w):
+ *                 (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * The router is fp32 in every case (Wg, bias and logits).
+ */
+typedef struct {
+    int64_t T, d, E, k, inter, inter_shared;
+    int32_t act_dtype, w_dtype;
+} moe_shape_t;
+
+/*
+ * Bytes of device workspace moe_route / moe_forward need for `shape` (a pure host function; 0 on an
+ * invalid shape).  The workspace must be 256-byte aligned.  Its contents need no initialisation and
+ * are undefined afterwards.
+ */
+size_t moe_workspace_size(const moe_shape_t* shape);
+
+/*
+ * Routing only: router logits, top-k, softmax and the expert-sorted permutation.
+ *   x            [T, d] act_dtype
+ *   Wg           [d, E] fp32 router weight (logits = x Wg)
+ *   bias         [E] fp32 logit bias added before selection, or NULL
+ *   idx    out   [T, k] int32 selected experts, descending logit, ties -> lower expert index
+ *   w      out   [T, k] fp32 softmax over the k selected logits
+ *   counts out   [E] int32 tokens routed to each expert (torch.bincount of idx)
+ *   offsets out  [E + 1] int32 exclusive prefix sum of counts
+ *   sorted_slots out [T * k] int32 slot ids t*k+j, expert by expert, tokens ascending within an expert
+ *   pos    out   [T * k] int32 inverse of sorted_slots, or NULL
+ * Logits are one fp32 fused-multiply-add chain per (token, expert) over i ascending, then one fp32 add
+ * of bias[e], so routing is a deterministic function of the inputs.
+ */
+moe_status_t moe_route(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                       int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                       int32_t* pos, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The whole layer: routing, routed SwiGLU experts, shared SwiGLU expert and the weighted combine.
+ *   x        [T, d] act_dtype (not modified; must not alias y)
+ *   Wg, bias as in moe_route
+ *   W1, W3   [E, inter, d] w_dtype (nn.Linear [out, in] layout: g = x W1^T per expert)
+ *   W2       [E, d, inter] w_dtype
+ *   S1, S3   [inter_shared, d] w_dtype;  S2 [d, inter_shared] w_dtype
+ *   W1s, W3s [E, inter/128, d/128] fp32, W2s [E, d/128, inter/128] fp32, S1s, S3s
+ *            [inter_shared/128, d/128] fp32, S2s [d/128, inter_shared/128] fp32: one scale per 128x128
+ *            weight block, value = code * scale.  Required iff w_dtype == MOE_FP8_E4M3, else ignored.
+ *   y    out [T, d] act_dtype
+ *   idx_out, w_out [T, k], counts_out [E]: optional copies of the routing (NULL to skip)
+ * Rounding: each linear's output is rounded to act_dtype; silu(g)*u is formed in fp32 and rounded to
+ * act_dtype; with fp8 weights, x and h are quantised per 1x128 group (s = amax/448, codes = E4M3
+ * round-to-nearest-even of v/s); the combine accumulates w * expert output and the shared output in
+ * fp32 in a fixed order and rounds once to act_dtype.  The result is bitwise deterministic.
+ */
+moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                         const void* W1, const void* W3, const void* W2,
+                         const float* W1s, const float* W3s, const float* W2s,
+                         const void* S1, const void* S3, const void* S2,
+                         const float* S1s, const float* S3s, const float* S2s,
+                         void* y, int32_t* idx_out, float* w_out, int32_t* counts_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_forward with stage timing: identical work and results, and events[i] (hipEvent_t, created by the
+ * caller) is recorded on `stream` before stage i and events[MOE_NUM_STAGES] after the last stage, so
+ * hipEventElapsedTime(events[i], events[i+1]) is the device time of stage i.  Stages, in order:
+ *   0 router logits, 1 top-k + softmax, 2 permutation and tile list, 3 x quantisation (fp8 weights
+ *   only; empty otherwise), 4 grouped up GEMM (W1, W3, SiLU*mul; routed and shared), 5 grouped down GEMM
+ *   (W2), 6 combine.
+ * events may be NULL (then it is moe_forward).
+ */
+#define MOE_NUM_STAGES 7
+moe_status_t moe_forward_staged(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                                const void* W1, const void* W3, const void* W2,
+                                const float* W1s, const float* W3s, const float* W2s,
+                                const void* S1, const void* S3, const void* S2,
+                                const float* S1s, const float* S3s, const float* S2s,
+                                void* y, int32_t* idx_out, float* w_out, int32_t* counts_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* events);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,463 @@
+// gemm.hip -- grouped expert GEMMs on CDNA4 MFMA.
+//
+// Expert math from "DeepSeek-V3.2-Exp / Mixture of experts / Shared expert" ("All 5 steps"):
+// g = x W1, u = x W3, a = g sigma(g), h = a (.) u, y = h W2; the MLP forward excerpt forms
+// silu(g) * u in fp32 from the linears' outputs and casts it back to the activation dtype before W2.
+// Each linear's output is rounded to the activation dtype, as a bf16 linear returns bf16.
+//
+// Work list.  Rows are the expert-sorted (token, slot) pairs of every routed expert followed by one
+// row per token for the shared expert (group E); the tile list cuts each group into BM-row tiles.
+// A block computes one (tile, n-block): rows of that group against BN output features.
+//   up   : A = x rows gathered through row_token, B = [W1 rows n0..n0+BN) ; W3 rows n0..n0+BN)],
+//          epilogue h = round(silu(round(g)) * round(u)) -> h rows (fp8 weights: E4M3 codes of h per
+//          1x128 group plus one scale per group);
+//   down : A = h rows (already in sorted order), B = W2 rows, epilogue y_rows = round(acc).
+// Empty experts create no tiles and read no weights.
+//
+// Data path.  A and B tiles are staged through LDS in 128-byte-per-row K stages (double buffered,
+// 16-byte chunks XOR-swizzled by row), fragments read with 16-byte LDS reads.  MFMA per element type:
+//   fp32 : v_mfma_f32_16x16x4_f32   (4 per 16-byte fragment; lane group q holds k = 4q + e)
+//   bf16 : v_mfma_f32_16x16x32_bf16 (one per 16-byte fragment)
+//   fp8  : v_mfma_scale_f32_16x16x128_f8f6f4 with unit exponent scales, one per 128-byte stage, whose
+//          fp32 result is multiplied by (activation scale of the row) * (weight block scale) and
+//          added to the accumulator: a 128-wide K stage is exactly one 128x128 weight block.
+// Since A and B fragments use the same lane -> k assignment, any consistent K permutation inside a
+// stage gives the same dot product.
+#include "moe_common.h"
+
+namespace moe {
+
+enum { ET_F32 = 0, ET_BF16 = 1, ET_FP8 = 2 };
+
+struct GemmArgs {
+    const int4* tiles;        // tile list
+    const int32_t* ntiles;    // number of valid tiles
+    const int32_t* row_token; // up: sorted row -> token (A row)
+    const uint8_t* A;         // up: x or its E4M3 codes; down: h
+    const float* As;          // fp8: scales of A rows per 128-K block ([rows, K/128])
+    int64_t lda;              // bytes between A rows
+    int64_t ldas;             // floats between rows of As
+    const uint8_t* B1;        // routed weights (up: W1, down: W2) [E, N, K]
+    const uint8_t* B3;        // up: W3
+    const float* B1s;         // fp8 block scales [E, N/128, K/128]
+    const float* B3s;
+    const uint8_t* S1;        // shared-expert weights [N_s, K_s]
+    const uint8_t* S3;
+    const float* S1s;
+    const float* S3s;
+    uint8_t* out;             // up: h; down: y_rows
+    float* outs;              // up with fp8: scales of h [rows, inter_max/128]
+    int64_t ldo;              // elements between output rows
+    int64_t ldos;             // floats between rows of outs
+    int E;
+    int N_r, N_s;             // output features: routed / shared
+    int K_r, K_s;             // reduction length: routed / shared
+    int n_blocks;             // n-blocks per tile (over the larger N)
+    int max_tiles;
+    int tile_major;           // 1: consecutive blocks walk tiles (weight reuse); 0: walk n-blocks
+};
+
+template <int ET> struct Elem;
+template <> struct Elem<ET_F32> { static constexpr int bytes = 4; };
+template <> struct Elem<ET_BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<ET_FP8> { static constexpr int bytes = 1; };
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    const float sig = 1.0f / (1.0f + expf(-g));
+    return (g * sig) * u;
+}
+
+// One K stage of MFMAs for a wave's WM x WN blocks (and the W3 half for the up GEMM).
+template <int ET, bool UP, int WM, int WN, int BN>
+__device__ __forceinline__ void mma_stage(const uint8_t* As_lds, const uint8_t* Bs_lds, const float* sA_lds,
+                                          float sb1, float sb3, int wm0, int wn0, int lane,
+                                          f32x4 (&acc1)[WM][WN], f32x4 (&acc3)[WM][WN])
+{
+    const int r16 = lane & 15, q = lane >> 4;
+    if constexpr (ET == ET_FP8) {
+        i32x8 a[WM], b1[WN], b3[WN];
+#pragma unroll
+        for (int i = 0; i < WM; i++) {
+            const int row = wm0 + i * 16 + r16;
+            const i32x4 lo = *(const i32x4*)(As_lds + swz(row, 2 * q));
+            const i32x4 hi = *(const i32x4*)(As_lds + swz(row, 2 * q + 1));
+            a[i] = (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
+#pragma unroll
+        for (int j = 0; j < WN; j++) {
+            const int row = wn0 + j * 16 + r16;
+            i32x4 lo = *(const i32x4*)(Bs_lds + swz(row, 2 * q));
+            i32x4 hi = *(const i32x4*)(Bs_lds + swz(row, 2 * q + 1));
+            b1[j] = (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (UP) {
+                lo = *(const i32x4*)(Bs_lds + swz(BN + row, 2 * q));
+                hi = *(const i32x4*)(Bs_lds + swz(BN + row, 2 * q + 1));
+                b3[j] = (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < WM; i++) {
+            float sa[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) sa[r] = sA_lds[wm0 + i * 16 + 4 * q + r];
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b1[j], zero, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc1[i][j][r] += p1[r] * (sa[r] * sb1);
+                if constexpr (UP) {
+                    const f32x4 p3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b3[j], zero, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * (sa[r] * sb3);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {          // two 64-byte K slices per stage
+            const int chunk = ks * 4 + q;
+            i32x4 a[WM], b1[WN], b3[WN];
+#pragma unroll
+            for (int i = 0; i < WM; i++) a[i] = *(const i32x4*)(As_lds + swz(wm0 + i * 16 + r16, chunk));
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                b1[j] = *(const i32x4*)(Bs_lds + swz(wn0 + j * 16 + r16, chunk));
+                if constexpr (UP) b3[j] = *(const i32x4*)(Bs_lds + swz(BN + wn0 + j * 16 + r16, chunk));
+            }
+#pragma unroll
+            for (int i = 0; i < WM; i++)
+#pragma unroll
+                for (int j = 0; j < WN; j++) {
+                    if constexpr (ET == ET_BF16) {
+                        acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                                             __builtin_bit_cast(bf16x8, b1[j]), acc1[i][j], 0, 0, 0);
+                        if constexpr (UP)
+                            acc3[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                                                 __builtin_bit_cast(bf16x8, b3[j]), acc3[i][j], 0, 0, 0);
+                    } else {
+                        const f32x4 af = __builtin_bit_cast(f32x4, a[i]), bf1 = __builtin_bit_cast(f32x4, b1[j]);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf1[e], acc1[i][j], 0, 0, 0);
+                        if constexpr (UP) {
+                            const f32x4 bf3 = __builtin_bit_cast(f32x4, b3[j]);
+#pragma unroll
+                            for (int e = 0; e < 4; e++) acc3[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf3[e], acc3[i][j], 0, 0, 0);
+                        }
+                    }
+                }
+        }
+    }
+}
+
+template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
+{
+    constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
+    constexpr int ROWS = BM + NB;                      // LDS rows per stage (128 bytes each)
+    constexpr int CHUNKS = ROWS * 8;                   // 16-byte chunks per stage
+    constexpr int PER = (CHUNKS + 255) / 256;          // chunks per thread
+    constexpr int WM = BM / 16 / WAVES_M, WN = BN / 16 / WAVES_N;
+    constexpr int KE = 128 / Elem<ET>::bytes;          // K elements per stage
+    constexpr bool FP8 = ET == ET_FP8;
+    static_assert(WAVES_M * WAVES_N == 4 && WM >= 1 && WN >= 1, "4 waves");
+    static_assert(!(FP8 && UP) || BN % 128 == 0, "fp8 h quantisation needs whole 128-column groups");
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * ROWS * 128];
+    __shared__ float sA[2][BM];
+    __shared__ int s_tok[BM];
+
+    // block -> (tile, n-block)
+    const int bid = blockIdx.x;
+    int tile, nb;
+    if (g.tile_major) { nb = bid / g.max_tiles; tile = bid % g.max_tiles; }
+    else { tile = bid / g.n_blocks; nb = bid % g.n_blocks; }
+    if (tile >= *g.ntiles) return;
+    const int4 td = g.tiles[tile];
+    const int grp = td.x, row0 = td.y, rows = td.z;
+    const bool shared = grp == g.E;
+    const int N = shared ? g.N_s : g.N_r, K = shared ? g.K_s : g.K_r;
+    const int n0 = nb * BN;
+    if (n0 >= N) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / WAVES_N) * WM * 16, wn0 = (wave % WAVES_N) * WN * 16;
+    const int64_t ldb = (int64_t)K * Elem<ET>::bytes;  // bytes per weight row
+    const uint8_t* W1 = shared ? g.S1 : g.B1 + (int64_t)grp * N * ldb;
+    const uint8_t* W3 = UP ? (shared ? g.S3 : g.B3 + (int64_t)grp * N * ldb) : nullptr;
+    const int nkb = K / 128;                           // fp8 weight blocks along K
+    const float* W1s = FP8 ? (shared ? g.S1s : g.B1s + (int64_t)grp * (N / 128) * nkb) + (n0 / 128) * nkb : nullptr;
+    const float* W3s = (FP8 && UP) ? (shared ? g.S3s : g.B3s + (int64_t)grp * (N / 128) * nkb) + (n0 / 128) * nkb : nullptr;
+
+    if (tid < BM) s_tok[tid] = tid < rows ? (UP ? g.row_token[row0 + tid] : row0 + tid) : -1;
+    __syncthreads();
+
+    // Per-thread source pointers of its chunks (fixed across K; advanced by 128 bytes per stage).
+    const uint8_t* src[PER];
+    int dst[PER];
+#pragma unroll
+    for (int p = 0; p < PER; p++) {
+        const int c = tid + p * 256;
+        src[p] = nullptr;
+        dst[p] = -1;
+        if (c < CHUNKS) {
+            const int row = c >> 3, ch = c & 7;
+            dst[p] = swz(row, ch);
+            if (row < BM) {
+                const int r = s_tok[row];
+                if (r >= 0) src[p] = g.A + (int64_t)r * g.lda + ch * 16;
+            } else if (row < BM + BN) {
+                src[p] = W1 + (int64_t)(n0 + row - BM) * ldb + ch * 16;
+            } else {
+                src[p] = W3 + (int64_t)(n0 + row - BM - BN) * ldb + ch * 16;
+            }
+        }
+    }
+    i32x4 reg[PER];
+    auto load_stage = [&](int s) {
+#pragma unroll
+        for (int p = 0; p < PER; p++) {
+            reg[p] = (i32x4){0, 0, 0, 0};
+            if (src[p]) reg[p] = *(const i32x4*)(src[p] + (int64_t)s * 128);
+        }
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < PER; p++)
+            if (dst[p] >= 0) *(i32x4*)(smem + buf * ROWS * 128 + dst[p]) = reg[p];
+    };
+    auto load_scales = [&](int s, int buf) {
+        if constexpr (FP8) {
+            if (tid < BM) {
+                const int r = s_tok[tid];
+                sA[buf][tid] = r >= 0 ? g.As[(int64_t)r * g.ldas + s] : 0.0f;
+            }
+        }
+    };
+
+    f32x4 acc1[WM][WN], acc3[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < WN; j++) acc1[i][j] = acc3[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int nstages = K / KE;
+    load_stage(0);
+    store_stage(0);
+    load_scales(0, 0);
+    __syncthreads();
+    for (int s = 0; s < nstages; s++) {
+        const int buf = s & 1;
+        if (s + 1 < nstages) load_stage(s + 1);
+        float sb1 = 0.f, sb3 = 0.f;
+        if constexpr (FP8) {
+            sb1 = W1s[s];
+            if constexpr (UP) sb3 = W3s[s];
+        }
+        mma_stage<ET, UP, WM, WN, BN>(smem + buf * ROWS * 128, smem + buf * ROWS * 128 + BM * 128, sA[buf], sb1, sb3,
+                                      wm0, wn0, lane, acc1, acc3);
+        if (s + 1 < nstages) {
+            store_stage(buf ^ 1);
+            load_scales(s + 1, buf ^ 1);
+        }
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------------------------------------
+    // Epilogue.  Accumulator layout (16x16 MFMA): lane holds rows 4*(lane/16) + r, column lane % 16.
+    // ---------------------------------------------------------------------------------------------
+    const int r16 = lane & 15, q = lane >> 4;
+    if constexpr (UP && FP8) {
+        float* hs = (float*)smem;                      // [BM][BN] h values, then quantised per 128 group
+#pragma unroll
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int j = 0; j < WN; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float gg = round_bf16(acc1[i][j][r]), uu = round_bf16(acc3[i][j][r]);
+                    hs[(wm0 + i * 16 + 4 * q + r) * BN + wn0 + j * 16 + r16] = round_bf16(silu_mul(gg, uu));
+                }
+        __syncthreads();
+        // 16 threads per (row, 128-column group), 8 columns each
+        constexpr int GROUPS = BM * (BN / 128);
+        for (int gi = tid >> 4; gi < GROUPS; gi += 16) {
+            const int row = gi / (BN / 128), grp128 = gi % (BN / 128);
+            const int sub = tid & 15;
+            const float* v = hs + row * BN + grp128 * 128 + sub * 8;
+            float amax = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+            if (row < rows) {
+                uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
+                uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+                const int64_t orow = row0 + row;
+                *(uint2*)(g.out + orow * g.ldo + n0 + grp128 * 128 + sub * 8) = make_uint2(lo, hi);
+                if (sub == 0) g.outs[orow * g.ldos + (n0 + grp128 * 128) / 128] = sc;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = wm0 + i * 16 + 4 * q + r;
+                if (row >= rows) continue;
+                const int64_t orow = row0 + row;
+#pragma unroll
+                for (int j = 0; j < WN; j++) {
+                    const int col = n0 + wn0 + j * 16 + r16;
+                    float v;
+                    if constexpr (UP) {
+                        const float gg = round_act<ACT_BF16>(acc1[i][j][r]), uu = round_act<ACT_BF16>(acc3[i][j][r]);
+                        v = silu_mul(gg, uu);
+                    } else {
+                        v = acc1[i][j][r];
+                    }
+                    if constexpr (ACT_BF16) ((uint16_t*)g.out)[orow * g.ldo + col] = f32_to_bf16(v);
+                    else ((float*)g.out)[orow * g.ldo + col] = v;
+                }
+            }
+    }
+}
+
+// fp8 activation quantisation of x: per row, per 128-column group, s = amax / 448 (1 if amax = 0),
+// codes = E4M3(round to nearest even)(x / s).  16 threads per group, 8 elements each.
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t ngroups, int d,
+                                                        uint8_t* __restrict__ xq, float* __restrict__ xs)
+{
+    const int64_t gi = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int sub = threadIdx.x & 15;
+    if (gi >= ngroups) return;                         // whole 16-lane groups exit together
+    const int64_t row = gi / (d / 128), col = (gi % (d / 128)) * 128 + sub * 8;
+    const uint4 raw = *(const uint4*)(x + row * d + col);
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        v[2 * e] = __uint_as_float(wv[e] << 16);
+        v[2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    const uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
+    const uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+    *(uint2*)(xq + row * d + col) = make_uint2(lo, hi);
+    if (sub == 0) xs[gi] = sc;
+}
+
+hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace& ws, hipStream_t stream)
+{
+    const int64_t ngroups = s.T * (s.d / 128);
+    act_quant_kernel<<<(unsigned)((ngroups + 15) / 16), 256, 0, stream>>>((const uint16_t*)x, ngroups, (int)s.d, ws.xq, ws.xs);
+    return hipGetLastError();
+}
+
+template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N>
+static void launch_one(GemmArgs a, hipStream_t stream)
+{
+    const int64_t nblk = (int64_t)a.n_blocks * a.max_tiles;
+    grouped_gemm_kernel<ET, UP, ACT_BF16, BM, BN, WAVES_M, WAVES_N><<<(unsigned)nblk, 256, 0, stream>>>(a);
+}
+
+// Common fields of both GEMMs' arguments.
+static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws)
+{
+    GemmArgs a = {};
+    a.tiles = ws.tiles;
+    a.ntiles = ws.sync;
+    a.max_tiles = (int)ws.max_tiles;
+    a.E = (int)s.E;
+    a.tile_major = tile_rows(s) > 16;
+    return a;
+}
+
+hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, const void* W3, const float* W1s,
+                          const float* W3s, const void* S1, const void* S3, const float* S1s, const float* S3s,
+                          const Workspace& ws, hipStream_t stream)
+{
+    const bool fp8 = s.w_dtype == MOE_FP8_E4M3, f32 = s.act_dtype == MOE_F32;
+    const int64_t act = f32 ? 4 : 2;
+    GemmArgs up = base_args(s, ws);
+    up.row_token = ws.row_token;
+    up.A = fp8 ? ws.xq : (const uint8_t*)x;
+    up.As = ws.xs;
+    up.lda = s.d * (fp8 ? 1 : act);
+    up.ldas = s.d / 128;
+    up.B1 = (const uint8_t*)W1;
+    up.B3 = (const uint8_t*)W3;
+    up.B1s = W1s;
+    up.B3s = W3s;
+    up.S1 = (const uint8_t*)S1;
+    up.S3 = (const uint8_t*)S3;
+    up.S1s = S1s;
+    up.S3s = S3s;
+    up.out = (uint8_t*)ws.h;
+    up.outs = ws.hs;
+    up.ldo = ws.inter_max;
+    up.ldos = ws.inter_max / 128;
+    up.N_r = (int)s.inter;
+    up.N_s = (int)s.inter_shared;
+    up.K_r = up.K_s = (int)s.d;
+    const bool small = tile_rows(s) == 16;
+    if (fp8) {
+        up.n_blocks = (int)(ws.inter_max / 128);
+        if (small) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
+        else launch_one<ET_FP8, true, true, 128, 128, 2, 2>(up, stream);
+    } else if (f32) {
+        up.n_blocks = (int)(ws.inter_max / 64);
+        if (small) launch_one<ET_F32, true, false, 16, 64, 1, 4>(up, stream);
+        else launch_one<ET_F32, true, false, 128, 64, 2, 2>(up, stream);
+    } else {
+        up.n_blocks = (int)(ws.inter_max / 64);
+        if (small) launch_one<ET_BF16, true, true, 16, 64, 1, 4>(up, stream);
+        else launch_one<ET_BF16, true, true, 128, 64, 2, 2>(up, stream);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W2s, const void* S2, const float* S2s,
+                            const Workspace& ws, hipStream_t stream)
+{
+    const bool fp8 = s.w_dtype == MOE_FP8_E4M3, f32 = s.act_dtype == MOE_F32;
+    const int64_t act = f32 ? 4 : 2;
+    GemmArgs dn = base_args(s, ws);
+    dn.A = (const uint8_t*)ws.h;
+    dn.As = ws.hs;
+    dn.lda = ws.inter_max * (fp8 ? 1 : act);
+    dn.ldas = ws.inter_max / 128;
+    dn.B1 = (const uint8_t*)W2;
+    dn.B1s = W2s;
+    dn.S1 = (const uint8_t*)S2;
+    dn.S1s = S2s;
+    dn.out = (uint8_t*)ws.y_rows;
+    dn.ldo = s.d;
+    dn.N_r = dn.N_s = (int)s.d;
+    dn.K_r = (int)s.inter;
+    dn.K_s = (int)s.inter_shared;
+    const bool small = tile_rows(s) == 16;
+    if (small) {
+        dn.n_blocks = (int)(s.d / 64);
+        if (fp8) launch_one<ET_FP8, false, true, 16, 64, 1, 4>(dn, stream);
+        else if (f32) launch_one<ET_F32, false, false, 16, 64, 1, 4>(dn, stream);
+        else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
+    } else {
+        dn.n_blocks = (int)(s.d / 128);
+        if (fp8) launch_one<ET_FP8, false, true, 128, 128, 2, 2>(dn, stream);
+        else if (f32) launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
+        else launch_one<ET_BF16, false, true, 128, 128, 2, 2>(dn, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

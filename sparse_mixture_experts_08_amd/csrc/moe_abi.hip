@@ -1,0 +1,183 @@
+// moe_abi.hip -- the C entry points of moe.h: argument validation, workspace layout and the launch
+// sequence of the layer (router -> top-k -> permutation -> [x quantisation] -> grouped up GEMM ->
+// grouped down GEMM -> combine), all enqueued on the caller's stream with no host synchronisation.
+#include <string.h>
+
+#include "moe_common.h"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int tile_rows(const moe_shape_t& s)
+{
+    // Small average group sizes (decode): 16-row tiles; otherwise 128-row tiles.
+    const int64_t per_expert = s.T * s.k / (s.E > 0 ? s.E : 1);
+    return per_expert <= 24 ? 16 : 128;
+}
+
+Workspace carve_workspace(const moe_shape_t& s, void* base)
+{
+    Workspace w;
+    memset(&w, 0, sizeof(w));
+    const int64_t T = s.T, E = s.E, k = s.k, d = s.d;
+    const int64_t rows = T * k + T;
+    const int bm = tile_rows(s);
+    w.nchunks = (T + 63) / 64;
+    w.max_tiles = rows / bm + E + 2;
+    w.inter_max = s.inter > s.inter_shared ? s.inter : s.inter_shared;
+    const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
+    const size_t act = s.act_dtype == MOE_F32 ? 4 : 2;
+    size_t off = 0;
+    char* b = (char*)base;
+    auto take = [&](size_t bytes) -> void* {
+        void* p = b ? (void*)(b + off) : nullptr;
+        off += align256(bytes);
+        return p;
+    };
+    w.logits = (float*)take(sizeof(float) * T * E);
+    w.idx = (int32_t*)take(sizeof(int32_t) * T * k);
+    w.w = (float*)take(sizeof(float) * T * k);
+    w.counts = (int32_t*)take(sizeof(int32_t) * E);
+    w.offsets = (int32_t*)take(sizeof(int32_t) * (E + 1));
+    w.chunk_counts = (int32_t*)take(sizeof(int32_t) * w.nchunks * E);
+    w.chunk_prefix = (int32_t*)take(sizeof(int32_t) * w.nchunks * E);
+    w.chunk_bits = (uint64_t*)take(sizeof(uint64_t) * w.nchunks * E);
+    w.sorted_slots = (int32_t*)take(sizeof(int32_t) * T * k);
+    w.pos = (int32_t*)take(sizeof(int32_t) * T * k);
+    w.row_token = (int32_t*)take(sizeof(int32_t) * rows);
+    w.tiles = (int4*)take(sizeof(int4) * w.max_tiles);
+    w.sync = (int32_t*)take(sizeof(int32_t) * 4);
+    if (fp8) {
+        w.xq = (uint8_t*)take((size_t)T * d);
+        w.xs = (float*)take(sizeof(float) * T * (d / 128));
+        w.h = take((size_t)rows * w.inter_max);
+        w.hs = (float*)take(sizeof(float) * rows * (w.inter_max / 128));
+    } else {
+        w.h = take(act * rows * w.inter_max);
+    }
+    w.y_rows = take(act * rows * d);
+    w.total = off;
+    return w;
+}
+
+// Host-side validation shared by both entry points.
+static moe_status_t check_shape(const moe_shape_t* s)
+{
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->inter <= 0 || s->inter_shared <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+    if (s->k > 16 || s->E > 1024) return MOE_ERR_UNSUPPORTED;
+    if (s->d % 128 || s->inter % 128 || s->inter_shared % 128) return MOE_ERR_UNSUPPORTED;
+    const bool ok = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||
+                    (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_BF16) ||
+                    (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8_E4M3);
+    if (!ok) return MOE_ERR_UNSUPPORTED;
+    // int32 indexing of rows and elements inside the kernels
+    if (s->T > (1 << 24) || (s->T * (s->k + 1)) * s->d > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_workspace_size(const moe_shape_t* shape)
+{
+    if (check_shape(shape) != MOE_OK) return 0;
+    return carve_workspace(*shape, nullptr).total;
+}
+
+extern "C" const char* moe_status_string(moe_status_t st)
+{
+    switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+#define MOE_TRY(expr)                                    \
+    do {                                                 \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP;    \
+    } while (0)
+
+extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                                  int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                                  int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream)
+{
+    moe_status_t st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape_t& s = *shape;
+    if (s.T == 0) return MOE_OK;
+    if (!x || !Wg || !idx || !w || !counts || !offsets || !sorted_slots || !workspace) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
+    Workspace ws = carve_workspace(s, workspace);
+    if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
+    MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
+    MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
+    MOE_TRY(launch_permute(s, idx, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws, tile_rows(s), stream));
+    return MOE_OK;
+}
+
+extern "C" moe_status_t moe_forward_staged(const moe_shape_t* shape, const void* x, const float* Wg,
+                                           const float* bias, const void* W1, const void* W3, const void* W2,
+                                           const float* W1s, const float* W3s, const float* W2s, const void* S1,
+                                           const void* S3, const void* S2, const float* S1s, const float* S3s,
+                                           const float* S2s, void* y, int32_t* idx_out, float* w_out,
+                                           int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream, hipEvent_t* events)
+{
+    moe_status_t st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape_t& s = *shape;
+    if (s.T == 0) return MOE_OK;
+    if (!x || !Wg || !W1 || !W3 || !W2 || !S1 || !S3 || !S2 || !y || !workspace) return MOE_ERR_INVALID_ARG;
+    const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
+    if (fp8 && (!W1s || !W3s || !W2s || !S1s || !S3s || !S2s)) return MOE_ERR_INVALID_ARG;
+    if (x == y) return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, W1, W3, W2, S1, S3, S2, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+    Workspace ws = carve_workspace(s, workspace);
+    if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
+
+    int32_t* idx = idx_out ? idx_out : ws.idx;
+    float* w = w_out ? w_out : ws.w;
+    int32_t* counts = counts_out ? counts_out : ws.counts;
+    auto mark = [&](int i) -> hipError_t { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
+    MOE_TRY(mark(0));
+    MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
+    MOE_TRY(mark(1));
+    MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
+    MOE_TRY(mark(2));
+    MOE_TRY(launch_permute(s, idx, counts, ws.offsets, ws.sorted_slots, ws.pos, ws, tile_rows(s), stream));
+    MOE_TRY(mark(3));
+    if (fp8) MOE_TRY(launch_act_quant(s, x, ws, stream));
+    MOE_TRY(mark(4));
+    MOE_TRY(launch_up_gemm(s, x, W1, W3, W1s, W3s, S1, S3, S1s, S3s, ws, stream));
+    MOE_TRY(mark(5));
+    MOE_TRY(launch_down_gemm(s, W2, W2s, S2, S2s, ws, stream));
+    MOE_TRY(mark(6));
+    MOE_TRY(launch_combine(s, ws.pos, w, ws, y, stream));
+    MOE_TRY(mark(7));
+    return MOE_OK;
+}
+
+extern "C" moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                                    const void* W1, const void* W3, const void* W2, const float* W1s,
+                                    const float* W3s, const float* W2s, const void* S1, const void* S3,
+                                    const void* S2, const float* S1s, const float* S3s, const float* S2s, void* y,
+                                    int32_t* idx_out, float* w_out, int32_t* counts_out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream)
+{
+    return moe_forward_staged(shape, x, Wg, bias, W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s, S2s, y, idx_out,
+                              w_out, counts_out, workspace, workspace_bytes, stream, nullptr);
+}

@@ -1,0 +1,97 @@
+// moe_common.h -- device helpers, workspace layout and kernel launchers shared by the HIP sources of
+// the MoE layer library (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------------------------
+// Scalar conversions (finite inputs).
+// ------------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to the nearest bf16 (ties to even) and return its bit pattern.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Round to the nearest bf16 (ties to even), returned as the (exact) float value.
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// Value rounded to the activation dtype (fp32: identity).
+template <bool ACT_BF16>
+__device__ __forceinline__ float round_act(float f) { return ACT_BF16 ? round_bf16(f) : f; }
+
+// Two floats -> two OCP E4M3 codes (round to nearest even; |v| <= 448 here), packed in the low 16 bits.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Vector types for 16-byte loads and MFMA operands.
+// ------------------------------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------------------------------------
+// Workspace layout.  Every region is 256-byte aligned; offsets are computed from the shape only.
+// ------------------------------------------------------------------------------------------------
+struct Workspace {
+    float* logits;          // [T, E] router logits
+    int32_t* idx;           // [T, k]
+    float* w;               // [T, k]
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E + 1]
+    int32_t* chunk_counts;  // [nchunks, E]  tokens of a 64-token chunk routed to each expert
+    int32_t* chunk_prefix;  // [nchunks, E]  exclusive prefix of chunk_counts over chunks, per expert
+    uint64_t* chunk_bits;   // [nchunks, E]  which of the chunk's 64 tokens chose each expert
+    int32_t* sorted_slots;  // [T * k]
+    int32_t* pos;           // [T * k]
+    int32_t* row_token;     // [T * k + T]  token of each expert-sorted row; shared rows last
+    int4* tiles;            // [max_tiles]  (group, first row, rows, 0); group E is the shared expert
+    int32_t* sync;          // [4]  tile count, completion ticket
+    uint8_t* xq;            // [T, d] E4M3 codes of x (fp8 weights only)
+    float* xs;              // [T, d / 128] their scales
+    void* h;                // [T * k + T, inter_max] act dtype, or E4M3 codes (fp8 weights)
+    float* hs;              // [T * k + T, inter_max / 128] (fp8 weights only)
+    void* y_rows;           // [T * k + T, d] act dtype: each row's expert output
+    size_t total;
+    int64_t max_tiles, nchunks, inter_max;
+};
+
+// Rows per grouped-GEMM tile for this shape.
+int tile_rows(const moe_shape_t& s);
+
+// Compute the layout (pointers relative to `base`; base may be null to size it).
+Workspace carve_workspace(const moe_shape_t& s, void* base);
+
+// ------------------------------------------------------------------------------------------------
+// Kernel launchers (all enqueue on `stream`, return hipGetLastError()).
+// ------------------------------------------------------------------------------------------------
+hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
+                                float* logits, hipStream_t stream);
+hipError_t launch_topk(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, const Workspace& ws,
+                       hipStream_t stream);
+hipError_t launch_permute(const moe_shape_t& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm, hipStream_t stream);
+hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace& ws, hipStream_t stream);
+hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, const void* W3, const float* W1s,
+                          const float* W3s, const void* S1, const void* S3, const float* S1s, const float* S3s,
+                          const Workspace& ws, hipStream_t stream);
+hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W2s, const void* S2, const float* S2s,
+                            const Workspace& ws, hipStream_t stream);
+hipError_t launch_combine(const moe_shape_t& s, const int32_t* pos, const float* w, const Workspace& ws, void* y,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,103 @@
+"""The C ABI of include/moe.h without a GPU: the library loads, exports what the header declares, sizes
+workspaces, and rejects bad arguments on the host before any launch (no device work is needed for that).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_08_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libmoe.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def _shape(**kw):
+    base = dict(T=64, d=7168, E=256, k=8, inter=2048, inter_shared=2048, act_dtype=B.MOE_BF16, w_dtype=B.MOE_BF16)
+    base.update(kw)
+    return B.make_shape(**base)
+
+
+def test_workspace_size_valid_shapes():
+    assert B.moe_workspace_size(_shape()) > 0
+    assert B.moe_workspace_size(_shape(T=0)) > 0
+    assert B.moe_workspace_size(_shape(act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, d=512, E=32, k=4, inter=256,
+                                       inter_shared=256)) > 0
+    assert 0 < B.moe_workspace_size(_shape(w_dtype=B.MOE_FP8_E4M3, T=32768)) < 8 << 30
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=0), dict(T=-1), dict(E=0), dict(k=9, E=8),                     # invalid
+    dict(k=17, E=64), dict(E=1025), dict(d=7100), dict(inter=2000),       # unsupported
+    dict(inter_shared=100), dict(act_dtype=B.MOE_F32),                    # (F32, BF16) pair
+    dict(act_dtype=B.MOE_FP8_E4M3, w_dtype=B.MOE_FP8_E4M3), dict(act_dtype=7),
+])
+def test_workspace_size_rejects_bad_shapes(kw):
+    assert B.moe_workspace_size(_shape(**kw)) == 0
+
+
+def _call_forward(shape, ptrs=None, ws_bytes=1 << 30):
+    L = B.lib()
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(20)] if ptrs is None else ptrs
+    return L.moe_forward(ctypes.byref(shape), *p, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_forward_argument_errors_are_host_side():
+    s = _shape()
+    # k > E, bad dtype pair, bad sizes: rejected before any pointer is touched
+    assert _call_forward(_shape(k=9, E=8)) == 1
+    assert _call_forward(_shape(d=7100)) == 2
+    assert _call_forward(_shape(act_dtype=B.MOE_F32)) == 2
+    # null required pointer
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(20)]
+    p[0] = None                                   # x
+    assert _call_forward(s, p) == 1
+    # y aliasing x
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(20)]
+    p[15] = p[0]
+    assert _call_forward(s, p) == 1
+    # misaligned weight pointer
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(20)]
+    p[3] = ctypes.c_void_p(0x1000 * 4 + 2)
+    assert _call_forward(s, p) == 1
+    # fp8 weights without scales
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(20)]
+    p[6] = None                                   # W1s
+    assert _call_forward(_shape(w_dtype=B.MOE_FP8_E4M3), p) == 1
+    # workspace too small, or misaligned
+    assert _call_forward(s, ws_bytes=1024) == 3
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(20)]
+    p[19] = ctypes.c_void_p(0x1000 * 20 + 16)
+    assert _call_forward(s, p) == 3
+
+
+def test_empty_input_is_a_no_op():
+    # T = 0: nothing to compute, nothing launched, any pointers accepted
+    assert _call_forward(_shape(T=0), [None] * 20, ws_bytes=0) == 0
+    L = B.lib()
+    assert L.moe_route(ctypes.byref(_shape(T=0)), *([None] * 10), ctypes.c_size_t(0), None) == 0
+
+
+def test_status_strings():
+    for st in range(5):
+        assert B.moe_status_string(st)
+    assert "workspace" in B.moe_status_string(3)
