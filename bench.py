@@ -9,6 +9,7 @@ around it on the launch stream, over the timed steps) and the CPU oracle timed o
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -73,6 +74,21 @@ def algorithmic(wl, counts):
                 layer_bytes=layer_bytes, layer_flops=up_flops + dn_flops + 2.0 * wl.T * wl.d * wl.E)
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it
+    was taken on the current GEMM source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "sparse_mixture_experts_08_amd", "csrc", "gemm.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec.get("gemm_source_sha256_16"):
+        return None
+    k = rec.get(kernel)
+    return None if not k else k["bytes"]
+
+
 def cpu_baseline(wl, inp, max_tokens):
     """The CPU oracle on a bounded sample of the same workload: routing of every token plus experts and
     combine for up to max_tokens tokens; tokens/s from the per-token cost of both parts."""
@@ -103,6 +119,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, one plain device copy of this many MiB (a known-size reference "
+                         "for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this layer runs unsharded on a single MI355X (asked for --gpus "
@@ -158,9 +177,17 @@ def main():
         roof = {"bound": "mfma", "achieved": alg["up_flops"] / (up_ms * 1e-3) / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[wl.w_dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl.name, "up_gemm")
     roof["kernel"] = "grouped up GEMM (W1, W3, SiLU*mul; routed + shared)"
     roof["kernel_ms"] = up_ms
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": "MoE-layer tokens/s at d=7168, 256 experts top-8; % of HBM or MFMA roofline",

@@ -122,8 +122,9 @@ moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const float* W
  * moe_forward with stage timing: identical work and results, and events[i] (hipEvent_t, created by the
  * caller) is recorded on `stream` before stage i and events[MOE_NUM_STAGES] after the last stage, so
  * hipEventElapsedTime(events[i], events[i+1]) is the device time of stage i.  Stages, in order:
- *   0 router logits, 1 top-k + softmax, 2 permutation and tile list, 3 x quantisation (fp8 weights
- *   only; empty otherwise), 4 grouped up GEMM (W1, W3, SiLU*mul; routed and shared), 5 grouped down GEMM
+ *   0 router logits, 1 top-k + softmax (with T <= 256 also the permutation and tile list, one launch),
+ *   2 permutation and tile list (empty when done in stage 1), 3 x quantisation (fp8 weights only;
+ *   empty otherwise), 4 grouped up GEMM (W1, W3, SiLU*mul; routed and shared), 5 grouped down GEMM
  *   (W2), 6 combine.
  * events may be NULL (then it is moe_forward).
  */

@@ -122,8 +122,13 @@ extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const
     Workspace ws = carve_workspace(s, workspace);
     if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
     MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
-    MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
-    MOE_TRY(launch_permute(s, idx, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws, tile_rows(s), stream));
+    if (routing_is_fused(s)) {
+        MOE_TRY(launch_routing_fused(s, ws.logits, idx, w, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws,
+                                     tile_rows(s), stream));
+    } else {
+        MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
+        MOE_TRY(launch_permute(s, idx, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws, tile_rows(s), stream));
+    }
     return MOE_OK;
 }
 
@@ -156,9 +161,15 @@ extern "C" moe_status_t moe_forward_staged(const moe_shape_t* shape, const void*
     MOE_TRY(mark(0));
     MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
     MOE_TRY(mark(1));
-    MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
-    MOE_TRY(mark(2));
-    MOE_TRY(launch_permute(s, idx, counts, ws.offsets, ws.sorted_slots, ws.pos, ws, tile_rows(s), stream));
+    if (routing_is_fused(s)) {
+        MOE_TRY(launch_routing_fused(s, ws.logits, idx, w, counts, ws.offsets, ws.sorted_slots, ws.pos, ws,
+                                     tile_rows(s), stream));
+        MOE_TRY(mark(2));
+    } else {
+        MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
+        MOE_TRY(mark(2));
+        MOE_TRY(launch_permute(s, idx, counts, ws.offsets, ws.sorted_slots, ws.pos, ws, tile_rows(s), stream));
+    }
     MOE_TRY(mark(3));
     if (fp8) MOE_TRY(launch_act_quant(s, x, ws, stream));
     MOE_TRY(mark(4));

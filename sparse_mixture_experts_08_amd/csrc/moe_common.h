@@ -36,6 +36,36 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Exclusive prefix sum of one int per thread over a block of NT threads (NT a multiple of 64, <= 1024).
+// `lds` holds NT/64 + 1 ints.  Returns the thread's exclusive prefix; *total gets the block sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* lds)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) lds[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < NT / 64; w++) {
+            const int t = lds[w];
+            lds[w] = run;
+            run += t;
+        }
+        lds[NT / 64] = run;
+    }
+    __syncthreads();
+    const int excl = x - v + lds[wave];
+    *total = lds[NT / 64];
+    __syncthreads();
+    return excl;
+}
+
 // ------------------------------------------------------------------------------------------------
 // Vector types for 16-byte loads and MFMA operands.
 // ------------------------------------------------------------------------------------------------
@@ -83,6 +113,10 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
                                 float* logits, hipStream_t stream);
 hipError_t launch_topk(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, const Workspace& ws,
                        hipStream_t stream);
+bool routing_is_fused(const moe_shape_t& s);
+hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm,
+                                hipStream_t stream);
 hipError_t launch_permute(const moe_shape_t& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm, hipStream_t stream);
 hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace& ws, hipStream_t stream);

@@ -2,49 +2,160 @@
 //
 // What it computes is what the MoE forward excerpt on "DeepSeek-V3.2-Exp / Mixture of experts" does on
 // the host: a bincount of the selected indices, then per expert the (token, slot) pairs that chose it,
-// tokens ascending (torch.where scans row-major).  Here it is three passes over 64-token chunks with no
-// host synchronisation and no order-dependent atomics:
-//   1. (in the top-k kernel) a 64-bit mask per (chunk, expert) of the chunk's tokens that chose it;
-//   2. one block per expert: exclusive prefix of the chunk counts; the last block to finish (a ticket
-//      counter) scans the expert counts into offsets and writes the tile list;
-//   3. one wavefront per chunk: a slot's position is offsets[e] + its chunk's prefix for e + the number
-//      of earlier tokens of the chunk in e's mask.
+// tokens ascending (torch.where scans row-major).  Here it runs on 64-token chunks with no host
+// synchronisation and no order-dependent atomics:
+//   - a 64-bit mask per (chunk, expert) of the chunk's tokens that chose it (built with the top-k);
+//   - counts = popcounts summed over chunks; offsets = exclusive scan of counts over experts;
+//   - a slot's position is offsets[e] + (tokens of earlier chunks in e) + (earlier tokens of its own
+//     chunk in e's mask), so positions are unique and ascending in token order within each expert.
 // Sorted rows [0, T*k) hold the routed slots; rows [T*k, T*k + T) are the shared expert's, token order.
+//
+// Two paths: up to 256 tokens, one block does top-k, masks, scans, scatter and tiles in one launch;
+// beyond that, a top-k kernel per chunk (router.hip), a per-expert scan whose last block writes offsets
+// and tiles, and a scatter kernel.
 #include "moe_common.h"
+#include "topk.h"
 
 namespace moe {
 
+constexpr int kFusedMaxTokens = 256;
+
+// Tile list for groups with counts cnt[0..E) and offsets off[0..E]: shared expert (group E, rows
+// [T*k, T*k + T)) first, then experts ascending, each cut into bm-row tiles.  One thread per expert;
+// called by all NT threads of the block.
+template <int NT>
+__device__ void write_tiles(const int* cnt, const int* off, int E, int T, int k, int bm, int4* tiles, int32_t* ntiles,
+                            int* scan_lds)
+{
+    const int nshared = (T + bm - 1) / bm;
+    for (int i = threadIdx.x; i < nshared; i += NT) tiles[i] = make_int4(E, T * k + i * bm, min(bm, T - i * bm), 0);
+    int carry = nshared;
+    for (int e0 = 0; e0 < E; e0 += NT) {
+        const int e = e0 + threadIdx.x;
+        const int c = e < E ? cnt[e] : 0;
+        const int nt = (c + bm - 1) / bm;
+        int total;
+        const int base = carry + block_exclusive_scan<NT>(nt, &total, scan_lds);
+        for (int r = 0, i = 0; r < c; r += bm, i++) tiles[base + i] = make_int4(e, off[e] + r, min(bm, c - r), 0);
+        carry += total;
+    }
+    if (threadIdx.x == 0) ntiles[0] = carry;
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Fused path (T <= 256): one block of 1024 threads.
+// ---------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restrict__ L, int T, int E, int k, int bm,
+                                                           int32_t* __restrict__ idx, float* __restrict__ w,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_slots, int32_t* __restrict__ pos,
+                                                           int32_t* __restrict__ row_token, int4* __restrict__ tiles,
+                                                           int32_t* __restrict__ sync)
+{
+    __shared__ uint32_t bits_lo[4][1024], bits_hi[4][1024];   // [chunk][expert]
+    __shared__ int cnt[1024], off[1025], cpre[4][1024];
+    __shared__ int idx_s[kFusedMaxTokens * 16];
+    __shared__ int scan_lds[17];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nch = (T + 63) / 64;
+    for (int i = tid; i < 4 * 1024; i += 1024) (&bits_lo[0][0])[i] = (&bits_hi[0][0])[i] = 0;
+    __syncthreads();
+
+    // top-k: 16 lanes per token when E <= 256, else a whole wavefront per token
+    if (E <= 256) {
+        const int g = lane >> 4, sub = lane & 15;
+        for (int t0 = wave * 4; t0 < T; t0 += 64) {
+            const int t = t0 + g;
+            const bool valid = t < T;
+            int my_e;
+            float my_w;
+            topk_group<16, 16>(L + (size_t)(valid ? t : 0) * E, E, k, sub, my_e, my_w);
+            if (valid && sub < k) {
+                idx[(size_t)t * k + sub] = my_e;
+                w[(size_t)t * k + sub] = my_w;
+                idx_s[t * k + sub] = my_e;
+                const int c = t >> 6, tl = t & 63;
+                if (tl < 32) atomicOr(&bits_lo[c][my_e], 1u << tl);
+                else atomicOr(&bits_hi[c][my_e], 1u << (tl - 32));
+            }
+        }
+    } else {
+        for (int t = wave; t < T; t += 16) {
+            int my_e;
+            float my_w;
+            topk_group<64, 16>(L + (size_t)t * E, E, k, lane, my_e, my_w);
+            if (lane < k) {
+                idx[(size_t)t * k + lane] = my_e;
+                w[(size_t)t * k + lane] = my_w;
+                idx_s[t * k + lane] = my_e;
+                const int c = t >> 6, tl = t & 63;
+                if (tl < 32) atomicOr(&bits_lo[c][my_e], 1u << tl);
+                else atomicOr(&bits_hi[c][my_e], 1u << (tl - 32));
+            }
+        }
+    }
+    __syncthreads();
+
+    // counts and per-chunk prefixes (one thread per expert)
+    int my_cnt = 0;
+    if (tid < E) {
+        for (int c = 0; c < nch; c++) {
+            cpre[c][tid] = my_cnt;
+            my_cnt += __popcll(((uint64_t)bits_hi[c][tid] << 32) | bits_lo[c][tid]);
+        }
+        cnt[tid] = my_cnt;
+    }
+    int total;
+    const int excl = block_exclusive_scan<1024>(tid < E ? my_cnt : 0, &total, scan_lds);
+    if (tid < E) {
+        off[tid] = excl;
+        counts[tid] = my_cnt;
+        offsets[tid] = excl;
+    }
+    if (tid == 0) {
+        off[E] = total;
+        offsets[E] = total;
+    }
+    __syncthreads();
+
+    // scatter
+    for (int s = tid; s < T * k; s += 1024) {
+        const int t = s / k, e = idx_s[s], c = t >> 6, tl = t & 63;
+        const uint64_t mask = ((uint64_t)bits_hi[c][e] << 32) | bits_lo[c][e];
+        const uint64_t below = tl ? (~0ull >> (64 - tl)) : 0ull;
+        const int p = off[e] + cpre[c][e] + __popcll(mask & below);
+        pos[s] = p;
+        sorted_slots[p] = s;
+        row_token[p] = t;
+    }
+    for (int t = tid; t < T; t += 1024) row_token[T * k + t] = t;
+    write_tiles<1024>(cnt, off, E, T, k, bm, tiles, sync, scan_lds);
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Multi-block path.
+// ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int E,
                                                          int T, int k, int bm, int32_t* __restrict__ chunk_prefix,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int4* __restrict__ tiles, int32_t* __restrict__ sync)
 {
-    __shared__ int32_t part[256];
-    __shared__ int32_t scan[1025];
+    __shared__ int scan_lds[5];
+    __shared__ int cnt[1024], off[1025];
     __shared__ int is_last;
     const int e = blockIdx.x, tid = threadIdx.x;
     const int per = (nchunks + 255) / 256;
     const int c0 = tid * per, c1 = min(c0 + per, nchunks);
     int sum = 0;
     for (int c = c0; c < c1; c++) sum += chunk_counts[(size_t)c * E + e];
-    part[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {          // 256 partial sums, scanned in order
-        int run = 0;
-        for (int i = 0; i < 256; i++) {
-            const int v = part[i];
-            part[i] = run;
-            run += v;
-        }
-        counts[e] = run;
-    }
-    __syncthreads();
-    int run = part[tid];
+    int total;
+    int run = block_exclusive_scan<256>(sum, &total, scan_lds);
     for (int c = c0; c < c1; c++) {
         const int v = chunk_counts[(size_t)c * E + e];
         chunk_prefix[(size_t)c * E + e] = run;
         run += v;
     }
+    if (tid == 0) counts[e] = total;
 
     // The last block to arrive sees every count: offsets and tile list.
     __threadfence();
@@ -53,37 +164,26 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t* __restri
     __syncthreads();
     if (!is_last) return;
     __threadfence();
-    for (int g = tid; g < E; g += 256) scan[g] = __hip_atomic_load(&counts[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (tid == 0) {          // exclusive scan of the counts, in expert order
-        int acc = 0;
-        for (int g = 0; g < E; g++) {
-            const int c = scan[g];
-            scan[g] = acc;
-            acc += c;
+    int carry = 0;
+    for (int g0 = 0; g0 < E; g0 += 256) {
+        const int g = g0 + tid;
+        const int c = g < E ? __hip_atomic_load(&counts[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        int tot;
+        const int ex = carry + block_exclusive_scan<256>(c, &tot, scan_lds);
+        if (g < E) {
+            cnt[g] = c;
+            off[g] = ex;
+            offsets[g] = ex;
         }
-        scan[E] = acc;       // == T * k
+        carry += tot;
     }
-    __syncthreads();
-    for (int g = tid; g <= E; g += 256) offsets[g] = scan[g];
-    // Tiles: shared expert (group E, rows [T*k, T*k+T)) first, then experts ascending.
-    __shared__ int tbase[1024];
-    const int nshared = (T + bm - 1) / bm;
     if (tid == 0) {
-        int nt = nshared;
-        for (int g = 0; g < E; g++) {
-            tbase[g] = nt;
-            nt += (scan[g + 1] - scan[g] + bm - 1) / bm;
-        }
-        sync[0] = nt;
+        off[E] = carry;
+        offsets[E] = carry;
         sync[1] = 0;
     }
     __syncthreads();
-    for (int i = tid; i < nshared; i += 256) tiles[i] = make_int4(E, T * k + i * bm, min(bm, T - i * bm), 0);
-    for (int g = tid; g < E; g += 256) {
-        const int c = scan[g + 1] - scan[g];
-        for (int r = 0; r < c; r += bm) tiles[tbase[g] + r / bm] = make_int4(g, scan[g] + r, min(bm, c - r), 0);
-    }
+    write_tiles<256>(cnt, off, E, T, k, bm, tiles, sync, scan_lds);
 }
 
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, const uint64_t* __restrict__ chunk_bits,
@@ -105,6 +205,17 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
         row_token[p] = t;
     }
     row_token[T * k + t] = t;
+}
+
+bool routing_is_fused(const moe_shape_t& s) { return s.T <= kFusedMaxTokens; }
+
+hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm,
+                                hipStream_t stream)
+{
+    route_fused_kernel<<<1, 1024, 0, stream>>>(logits, (int)s.T, (int)s.E, (int)s.k, bm, idx, w, counts, offsets,
+                                               sorted_slots, pos, ws.row_token, ws.tiles, ws.sync);
+    return hipGetLastError();
 }
 
 hipError_t launch_permute(const moe_shape_t& s, const int32_t* idx, int32_t* counts, int32_t* offsets,

@@ -13,6 +13,7 @@
 // the logit, then the complemented expert index), so a wave-wide max picks the largest logit and, among
 // equal logits, the lower expert index.  k rounds give the experts in descending-logit order.
 #include "moe_common.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -20,6 +21,24 @@ namespace moe {
 template <typename XT> __device__ __forceinline__ float ldx(const XT* p);
 template <> __device__ __forceinline__ float ldx<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ldx<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// Eight consecutive x elements (16-byte aligned for bf16, 32-byte for fp32) as floats.
+__device__ __forceinline__ void ldx8(const uint16_t* p, float* v)
+{
+    const uint4 r = *(const uint4*)p;
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        v[2 * j] = __uint_as_float(w[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void ldx8(const float* p, float* v)
+{
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
 // L[t][e] = fma chain over i of x[t][i] * Wg[i][e] (+ bias[e]).
 // Block tile BT tokens x BE experts, thread tile RT x RE, K staged through LDS in BK steps.
@@ -80,17 +99,110 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
     }
 }
 
+// Few tokens: one chain per lane.  Block = 16 tokens x 16 experts, 4 wavefronts (wave w: tokens
+// 4w..4w+3; lane (tt, el) = (lane / 16, lane % 16)).  Per 128-wide K stage the block loads the Wg tile
+// [128 i][16 e] (64-byte row segments) and the x tile [16 t][128 i] and stores them in LDS transposed
+// ([e][i], [t][i]) so each lane reads four consecutive i of its expert and of its token with one 16-byte
+// LDS read.  Global loads run two stages ahead of the FMAs (two register sets, loop unrolled by two).
+template <typename XT>
+__global__ __launch_bounds__(256) void router_logits_few_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
+                                                                const float* __restrict__ bias, float* __restrict__ L,
+                                                                int T, int d, int E, int vec)
+{
+    constexpr int BK = 128, PAD = 4;
+    __shared__ __attribute__((aligned(16))) float wT[2][16][BK + PAD];
+    __shared__ __attribute__((aligned(16))) float xT[2][16][BK + PAD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tt = wave * 4 + (lane >> 4), el = lane & 15;
+    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+    const int wr_row = tid >> 1, wr_col = (tid & 1) * 8;       // Wg tile element loaded by this thread
+    const int xr_tok = tid >> 4, xr_i = (tid & 15) * 8;        // x tile element loaded by this thread
+
+    struct Regs {
+        float4 w0, w1;
+        float x[8];
+    };
+    auto load = [&](Regs& r, int k0) {
+        const float* row = Wg + (size_t)(k0 + wr_row) * E + e0 + wr_col;
+        if (vec) {
+            r.w0 = *(const float4*)row;
+            r.w1 = *(const float4*)(row + 4);
+        } else {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = e0 + wr_col + j < E ? row[j] : 0.f;
+            r.w0 = make_float4(v[0], v[1], v[2], v[3]);
+            r.w1 = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        if (t0 + xr_tok < T) {
+            ldx8(x + (size_t)(t0 + xr_tok) * d + k0 + xr_i, r.x);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) r.x[j] = 0.f;
+        }
+    };
+    auto store = [&](const Regs& r, int b) {
+        wT[b][wr_col + 0][wr_row] = r.w0.x;
+        wT[b][wr_col + 1][wr_row] = r.w0.y;
+        wT[b][wr_col + 2][wr_row] = r.w0.z;
+        wT[b][wr_col + 3][wr_row] = r.w0.w;
+        wT[b][wr_col + 4][wr_row] = r.w1.x;
+        wT[b][wr_col + 5][wr_row] = r.w1.y;
+        wT[b][wr_col + 6][wr_row] = r.w1.z;
+        wT[b][wr_col + 7][wr_row] = r.w1.w;
+        *(float4*)&xT[b][xr_tok][xr_i] = make_float4(r.x[0], r.x[1], r.x[2], r.x[3]);
+        *(float4*)&xT[b][xr_tok][xr_i + 4] = make_float4(r.x[4], r.x[5], r.x[6], r.x[7]);
+    };
+    float acc = 0.0f;
+    auto compute = [&](int b) {
+#pragma unroll 8
+        for (int i = 0; i < BK; i += 4) {
+            const float4 a = *(const float4*)&xT[b][tt][i];
+            const float4 w = *(const float4*)&wT[b][el][i];
+            acc = __builtin_fmaf(a.x, w.x, acc);
+            acc = __builtin_fmaf(a.y, w.y, acc);
+            acc = __builtin_fmaf(a.z, w.z, acc);
+            acc = __builtin_fmaf(a.w, w.w, acc);
+        }
+    };
+
+    const int ns = d / BK;
+    Regs ra, rb;
+    load(ra, 0);
+    if (ns > 1) load(rb, BK);
+    store(ra, 0);
+    __syncthreads();
+    for (int s = 0; s < ns; s += 2) {
+        // stage s is in LDS buffer 0; rb holds stage s + 1 (in flight)
+        if (s + 2 < ns) load(ra, (s + 2) * BK);
+        compute(0);
+        if (s + 1 >= ns) break;
+        store(rb, 1);
+        __syncthreads();
+        // stage s + 1 is in LDS buffer 1; ra holds stage s + 2 (in flight)
+        if (s + 3 < ns) load(rb, (s + 3) * BK);
+        compute(1);
+        if (s + 2 < ns) store(ra, 0);
+        __syncthreads();
+    }
+    const int t = t0 + tt, e = e0 + el;
+    if (t < T && e < E) {
+        if (bias) acc = acc + bias[e];
+        L[(size_t)t * E + e] = acc;
+    }
+}
+
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
                                 float* logits, hipStream_t stream)
 {
     const int T = (int)s.T, d = (int)s.d, E = (int)s.E;
     const bool bf = s.act_dtype == MOE_BF16;
     if (T <= 512) {
-        dim3 grid((E + 63) / 64, (T + 3) / 4);
+        const int vec = (E % 16 == 0) && (((uintptr_t)Wg & 15) == 0);
+        dim3 grid((E + 15) / 16, (T + 15) / 16);
         if (bf)
-            router_logits_kernel<uint16_t, 4, 64, 1, 1, 64><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            router_logits_few_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E, vec);
         else
-            router_logits_kernel<float, 4, 64, 1, 1, 64><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            router_logits_few_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E, vec);
     } else {
         dim3 grid((E + 63) / 64, (T + 63) / 64);
         if (bf)
@@ -102,86 +214,35 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
 }
 
 // ------------------------------------------------------------------------------------------------
-// Top-k + softmax, one wavefront per token, 64 tokens (one chunk) per block of 4 wavefronts.
-// Also records, per chunk, which tokens chose each expert (a 64-bit mask) and how many did.
+// Top-k + softmax for many tokens: one wavefront per token, 64 tokens (one chunk) per block of 16
+// wavefronts.  Also records, per chunk, which tokens chose each expert (a 64-bit mask) and how many.
 // ------------------------------------------------------------------------------------------------
-
-// Order-preserving map of a finite float to uint32 (+0 and -0 map to the same key).
-__device__ __forceinline__ uint32_t ordered_bits(float f)
-{
-    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off, 64), hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ L, int T, int E, int k,
-                                                           int32_t* __restrict__ idx, float* __restrict__ w,
-                                                           uint64_t* __restrict__ chunk_bits,
-                                                           int32_t* __restrict__ chunk_counts,
-                                                           int32_t* __restrict__ sync)
+__global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restrict__ L, int T, int E, int k,
+                                                            int32_t* __restrict__ idx, float* __restrict__ w,
+                                                            uint64_t* __restrict__ chunk_bits,
+                                                            int32_t* __restrict__ chunk_counts,
+                                                            int32_t* __restrict__ sync)
 {
     __shared__ uint32_t bits_lo[1024], bits_hi[1024];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = blockIdx.x;
     if (c == 0 && threadIdx.x < 4) sync[threadIdx.x] = 0;   // reset the permutation's counters
-    for (int e = threadIdx.x; e < E; e += 256) bits_lo[e] = bits_hi[e] = 0;
+    for (int e = threadIdx.x; e < E; e += 1024) bits_lo[e] = bits_hi[e] = 0;
     __syncthreads();
-
-    const int nq = (E + 63) / 64;   // logits per lane (<= 16)
-    for (int tl = wave; tl < 64; tl += 4) {
+    for (int tl = wave; tl < 64; tl += 16) {
         const int t = c * 64 + tl;
         if (t >= T) break;
-        uint64_t key[16];
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-            const int e = lane + 64 * q;
-            key[q] = 0;
-            if (q < nq && e < E)
-                key[q] = ((uint64_t)ordered_bits(L[(size_t)t * E + e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-        }
-        int my_e = 0;
-        float my_l = 0.0f;
-        for (int j = 0; j < k; j++) {
-            uint64_t best = 0;
-#pragma unroll
-            for (int q = 0; q < 16; q++) best = key[q] > best ? key[q] : best;
-            best = wave_max_u64(best);
-            const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-            if ((e & 63) == lane) {
-#pragma unroll
-                for (int q = 0; q < 16; q++)
-                    if (q == (e >> 6)) key[q] = 0;
-            }
-            if (lane == j) {
-                my_e = e;
-                my_l = L[(size_t)t * E + e];
-            }
-        }
-        // softmax over the k selected logits; the first one is the largest
-        const float m = __shfl(my_l, 0, 64);
-        float z = lane < k ? expf(my_l - m) : 0.0f;
-        float sum = z;
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);   // lanes 0..15, fixed tree
-        sum = __shfl(sum, 0, 64);
+        int my_e;
+        float my_w;
+        topk_group<64, 16>(L + (size_t)t * E, E, k, lane, my_e, my_w);
         if (lane < k) {
             idx[(size_t)t * k + lane] = my_e;
-            w[(size_t)t * k + lane] = z / sum;
+            w[(size_t)t * k + lane] = my_w;
             if (tl < 32) atomicOr(&bits_lo[my_e], 1u << tl);
             else atomicOr(&bits_hi[my_e], 1u << (tl - 32));
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
+    for (int e = threadIdx.x; e < E; e += 1024) {
         const uint64_t b = ((uint64_t)bits_hi[e] << 32) | bits_lo[e];
         chunk_bits[(size_t)c * E + e] = b;
         chunk_counts[(size_t)c * E + e] = __popcll(b);
@@ -191,8 +252,8 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 hipError_t launch_topk(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, const Workspace& ws,
                        hipStream_t stream)
 {
-    topk_softmax_kernel<<<(unsigned)ws.nchunks, 256, 0, stream>>>(logits, (int)s.T, (int)s.E, (int)s.k, idx, w,
-                                                                    ws.chunk_bits, ws.chunk_counts, ws.sync);
+    topk_softmax_kernel<<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, (int)s.T, (int)s.E, (int)s.k, idx, w,
+                                                                     ws.chunk_bits, ws.chunk_counts, ws.sync);
     return hipGetLastError();
 }
 

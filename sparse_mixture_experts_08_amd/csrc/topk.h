@@ -1,0 +1,81 @@
+// topk.h -- top-k selection with a softmax over the selected logits, for one token held by a group of
+// lanes of a wavefront (gate of "DeepSeek-V3's mixture-of-experts architecture explained", block
+// pseudocode: topk of the router logits, then softmax over those k values).
+//
+// Each logit becomes a 64-bit key: its order-preserving bit pattern (+0 and -0 equal) in the high word
+// and the complemented expert index in the low word, so the maximum key is the largest logit and,
+// among equal logits, the lowest expert index.  k rounds of a group-wide maximum give the experts in
+// descending-logit order.  The softmax subtracts the first (largest) selected logit, exponentiates in
+// fp32 and divides by a fixed-order sum.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint32_t ordered_bits(float f)
+{
+    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t logit_key(float l, int e)
+{
+    return ((uint64_t)ordered_bits(l) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+// Maximum of a 64-bit value over groups of W consecutive lanes.
+template <int W>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = W / 2; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, off, W), hi = __shfl_xor((uint32_t)(v >> 32), off, W);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Top-k of row L[0..E) held by a group of W lanes (sub = lane index in the group), each lane holding the
+// logits e = sub + W * q for q < NQ (NQ * W >= E).  On return, lane sub < k of the group holds slot
+// sub's expert and weight.  k <= min(W, 16).
+template <int W, int NQ>
+__device__ __forceinline__ void topk_group(const float* __restrict__ Lrow, int E, int k, int sub, int& my_e, float& my_w)
+{
+    uint64_t key[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; q++) {
+        const int e = sub + W * q;
+        key[q] = e < E ? logit_key(Lrow[e], e) : 0ull;
+    }
+    my_e = 0;
+    float my_l = 0.0f;
+    for (int j = 0; j < k; j++) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int q = 0; q < NQ; q++) best = key[q] > best ? key[q] : best;
+        best = group_max_u64<W>(best);
+        const int e = key_expert(best);
+        if (e % W == sub) {
+#pragma unroll
+            for (int q = 0; q < NQ; q++)
+                if (q == e / W) key[q] = 0ull;
+        }
+        if (sub == j) {
+            my_e = e;
+            my_l = Lrow[e];
+        }
+    }
+    const float m = __shfl(my_l, 0, W);
+    const float z = sub < k ? expf(my_l - m) : 0.0f;
+    float sum = z;
+#pragma unroll
+    for (int off = (W < 16 ? W : 16) / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, W);
+    sum = __shfl(sum, 0, W);
+    my_w = z / sum;
+}
+
+}  // namespace moe
