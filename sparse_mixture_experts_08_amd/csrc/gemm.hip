@@ -78,14 +78,8 @@ __device__ __forceinline__ void mma_stage(const uint8_t* As_lds, const uint8_t* 
 {
     const int r16 = lane & 15, q = lane >> 4;
     if constexpr (ET == ET_FP8) {
-        i32x8 a[WM], b1[WN], b3[WN];
-#pragma unroll
-        for (int i = 0; i < WM; i++) {
-            const int row = wm0 + i * 16 + r16;
-            const i32x4 lo = *(const i32x4*)(As_lds + swz(row, 2 * q));
-            const i32x4 hi = *(const i32x4*)(As_lds + swz(row, 2 * q + 1));
-            a[i] = (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        }
+        // B fragments of the whole stage stay in registers; A fragments are read one row block at a time.
+        i32x8 b1[WN], b3[WN];
 #pragma unroll
         for (int j = 0; j < WN; j++) {
             const int row = wn0 + j * 16 + r16;
@@ -100,19 +94,27 @@ __device__ __forceinline__ void mma_stage(const uint8_t* As_lds, const uint8_t* 
         }
 #pragma unroll
         for (int i = 0; i < WM; i++) {
-            float sa[4];
+            const int row = wm0 + i * 16 + r16;
+            const i32x4 lo = *(const i32x4*)(As_lds + swz(row, 2 * q));
+            const i32x4 hi = *(const i32x4*)(As_lds + swz(row, 2 * q + 1));
+            const i32x8 a = (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            float s1[4], s3[4];
 #pragma unroll
-            for (int r = 0; r < 4; r++) sa[r] = sA_lds[wm0 + i * 16 + 4 * q + r];
+            for (int r = 0; r < 4; r++) {
+                const float sa = sA_lds[wm0 + i * 16 + 4 * q + r];
+                s1[r] = sa * sb1;
+                s3[r] = sa * sb3;
+            }
 #pragma unroll
             for (int j = 0; j < WN; j++) {
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b1[j], zero, 0, 0, 0, 127, 0, 127);
+                const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b1[j], zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                for (int r = 0; r < 4; r++) acc1[i][j][r] += p1[r] * (sa[r] * sb1);
+                for (int r = 0; r < 4; r++) acc1[i][j][r] += p1[r] * s1[r];
                 if constexpr (UP) {
-                    const f32x4 p3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b3[j], zero, 0, 0, 0, 127, 0, 127);
+                    const f32x4 p3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                    for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * (sa[r] * sb3);
+                    for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * s3[r];
                 }
             }
         }
@@ -153,8 +155,11 @@ __device__ __forceinline__ void mma_stage(const uint8_t* As_lds, const uint8_t* 
     }
 }
 
-template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
+// NBUF: LDS stages (2 = double buffered, one barrier per K stage; 1 = single buffer, two barriers per
+// stage but half the LDS, so two blocks share a CU and cover each other's barriers).  MINW: minimum
+// wavefronts per SIMD the register allocation must allow.
+template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, int MINW>
+__global__ __launch_bounds__(256, MINW) void grouped_gemm_kernel(GemmArgs g)
 {
     constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
     constexpr int ROWS = BM + NB;                      // LDS rows per stage (128 bytes each)
@@ -166,8 +171,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
     static_assert(WAVES_M * WAVES_N == 4 && WM >= 1 && WN >= 1, "4 waves");
     static_assert(!(FP8 && UP) || BN % 128 == 0, "fp8 h quantisation needs whole 128-column groups");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * ROWS * 128];
-    __shared__ float sA[2][BM];
+    static_assert(!(FP8 && UP) || BM * BN * 4 <= NBUF * ROWS * 128, "h tile must fit the staging LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * ROWS * 128];
+    __shared__ float sA[NBUF][BM];
     __shared__ int s_tok[BM];
 
     // block -> (tile, n-block)
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
     load_scales(0, 0);
     __syncthreads();
     for (int s = 0; s < nstages; s++) {
-        const int buf = s & 1;
+        const int buf = NBUF == 2 ? (s & 1) : 0;
         if (s + 1 < nstages) load_stage(s + 1);
         float sb1 = 0.f, sb3 = 0.f;
         if constexpr (FP8) {
@@ -259,9 +265,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
         }
         mma_stage<ET, UP, WM, WN, BN>(smem + buf * ROWS * 128, smem + buf * ROWS * 128 + BM * 128, sA[buf], sb1, sb3,
                                       wm0, wn0, lane, acc1, acc3);
+        if constexpr (NBUF == 1) __syncthreads();
         if (s + 1 < nstages) {
-            store_stage(buf ^ 1);
-            load_scales(s + 1, buf ^ 1);
+            store_stage(NBUF == 2 ? buf ^ 1 : 0);
+            load_scales(s + 1, NBUF == 2 ? buf ^ 1 : 0);
         }
         __syncthreads();
     }
@@ -363,12 +370,29 @@ hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace
     return hipGetLastError();
 }
 
-template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N, int NBUF = 2, int MINW = 1>
 static void launch_one(GemmArgs a, hipStream_t stream)
 {
     const int64_t nblk = (int64_t)a.n_blocks * a.max_tiles;
-    grouped_gemm_kernel<ET, UP, ACT_BF16, BM, BN, WAVES_M, WAVES_N><<<(unsigned)nblk, 256, 0, stream>>>(a);
+    grouped_gemm_kernel<ET, UP, ACT_BF16, BM, BN, WAVES_M, WAVES_N, NBUF, MINW><<<(unsigned)nblk, 256, 0, stream>>>(a);
 }
+
+// Output features per block for the 128- and 256-row tile classes.
+#ifndef MOE_MID_UP_BN
+#define MOE_MID_UP_BN 128
+#endif
+#ifndef MOE_MID_DN_BN
+#define MOE_MID_DN_BN 256
+#endif
+#ifndef MOE_MID_NBUF
+#define MOE_MID_NBUF 1
+#endif
+#ifndef MOE_MID_MINW
+#define MOE_MID_MINW 2
+#endif
+#ifndef MOE_BIG_DN_BN
+#define MOE_BIG_DN_BN 256
+#endif
 
 // Common fields of both GEMMs' arguments.
 static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws)
@@ -409,19 +433,26 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     up.N_r = (int)s.inter;
     up.N_s = (int)s.inter_shared;
     up.K_r = up.K_s = (int)s.d;
-    const bool small = tile_rows(s) == 16;
+    const int bm = tile_rows(s);
     if (fp8) {
         up.n_blocks = (int)(ws.inter_max / 128);
-        if (small) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
+        if (bm == 16) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
         else launch_one<ET_FP8, true, true, 128, 128, 2, 2>(up, stream);
     } else if (f32) {
         up.n_blocks = (int)(ws.inter_max / 64);
-        if (small) launch_one<ET_F32, true, false, 16, 64, 1, 4>(up, stream);
+        if (bm == 16) launch_one<ET_F32, true, false, 16, 64, 1, 4>(up, stream);
         else launch_one<ET_F32, true, false, 128, 64, 2, 2>(up, stream);
     } else {
-        up.n_blocks = (int)(ws.inter_max / 64);
-        if (small) launch_one<ET_BF16, true, true, 16, 64, 1, 4>(up, stream);
-        else launch_one<ET_BF16, true, true, 128, 64, 2, 2>(up, stream);
+        if (bm == 16) {
+            up.n_blocks = (int)(ws.inter_max / 64);
+            launch_one<ET_BF16, true, true, 16, 64, 1, 4>(up, stream);
+        } else if (bm == 128) {
+            up.n_blocks = (int)(ws.inter_max / MOE_MID_UP_BN);
+            launch_one<ET_BF16, true, true, 128, MOE_MID_UP_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(up, stream);
+        } else {
+            up.n_blocks = (int)(ws.inter_max / 128);
+            launch_one<ET_BF16, true, true, 256, 128, 2, 2>(up, stream);
+        }
     }
     return hipGetLastError();
 }
@@ -445,17 +476,26 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     dn.N_r = dn.N_s = (int)s.d;
     dn.K_r = (int)s.inter;
     dn.K_s = (int)s.inter_shared;
-    const bool small = tile_rows(s) == 16;
-    if (small) {
+    const int bm = tile_rows(s);
+    if (bm == 16) {
         dn.n_blocks = (int)(s.d / 64);
         if (fp8) launch_one<ET_FP8, false, true, 16, 64, 1, 4>(dn, stream);
         else if (f32) launch_one<ET_F32, false, false, 16, 64, 1, 4>(dn, stream);
         else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
+    } else if (bm == 128) {
+        if (fp8) {
+            dn.n_blocks = (int)(s.d / 128);
+            launch_one<ET_FP8, false, true, 128, 128, 2, 2>(dn, stream);
+        } else if (f32) {
+            dn.n_blocks = (int)(s.d / 128);
+            launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
+        } else {
+            dn.n_blocks = (int)(s.d / MOE_MID_DN_BN);
+            launch_one<ET_BF16, false, true, 128, MOE_MID_DN_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(dn, stream);
+        }
     } else {
-        dn.n_blocks = (int)(s.d / 128);
-        if (fp8) launch_one<ET_FP8, false, true, 128, 128, 2, 2>(dn, stream);
-        else if (f32) launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
-        else launch_one<ET_BF16, false, true, 128, 128, 2, 2>(dn, stream);
+        dn.n_blocks = (int)(s.d / MOE_BIG_DN_BN);
+        launch_one<ET_BF16, false, true, 256, MOE_BIG_DN_BN, 2, 2>(dn, stream);
     }
     return hipGetLastError();
 }

@@ -7,13 +7,21 @@
 
 namespace moe {
 
+#ifndef MOE_MAX_TILE_ROWS
+#define MOE_MAX_TILE_ROWS 128
+#endif
+
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int tile_rows(const moe_shape_t& s)
 {
-    // Small average group sizes (decode): 16-row tiles; otherwise 128-row tiles.
+    // By the average rows per routed expert: decode-sized groups -> 16-row tiles (weight streaming);
+    // ~100-200 rows -> 128-row tiles; larger groups -> 256-row tiles (more MFMA work per byte staged).
     const int64_t per_expert = s.T * s.k / (s.E > 0 ? s.E : 1);
-    return per_expert <= 24 ? 16 : 128;
+    if (per_expert <= 24) return 16;
+    // fp8 keeps 128-row tiles: its per-K-block scaling accumulates in VGPRs, which caps the per-wave tile.
+    if (per_expert <= 192 || s.act_dtype == MOE_F32 || s.w_dtype == MOE_FP8_E4M3) return 128;
+    return MOE_MAX_TILE_ROWS;
 }
 
 Workspace carve_workspace(const moe_shape_t& s, void* base)

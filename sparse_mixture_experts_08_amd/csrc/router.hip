@@ -5,9 +5,9 @@
 // logits; a softmax over those selected values only.
 //
 // Logits.  Each logit is one fp32 fused-multiply-add chain over i ascending, starting from +0.0f, then
-// one fp32 add of the optional bias.  The kernel is a register-tiled fp32 GEMM whose K loop runs in
-// order with no split, so every (token, expert) output keeps exactly that chain and the routing decision
-// is a deterministic function of x, Wg and bias.
+// one fp32 add of the optional bias.  Both kernels below are fp32 GEMMs whose K loop runs in order with
+// no split, so every (token, expert) output keeps exactly that chain and the routing decision is a
+// deterministic function of x, Wg and bias.
 //
 // Top-k.  One wavefront per token; each lane holds E/64 logits as 64-bit keys (order-preserving bits of
 // the logit, then the complemented expert index), so a wave-wide max picks the largest logit and, among
@@ -40,57 +40,87 @@ __device__ __forceinline__ void ldx8(const float* p, float* v)
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// L[t][e] = fma chain over i of x[t][i] * Wg[i][e] (+ bias[e]).
-// Block tile BT tokens x BE experts, thread tile RT x RE, K staged through LDS in BK steps.
-template <typename XT, int BT, int BE, int RT, int RE, int BK>
-__global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
-                                                            const float* __restrict__ bias, float* __restrict__ L,
-                                                            int T, int d, int E)
+// Many tokens: L[t][e] = fma chain over i of x[t][i] * Wg[i][e] (+ bias[e]).  Block tile 64 tokens x
+// 64 experts, thread tile 4 x 4, K staged through double-buffered LDS 32 at a time (the next stage's
+// global loads are in flight during the current stage's FMAs).  x is stored transposed ([i][t]) with
+// consecutive lanes on consecutive tokens, so the transposing stores and the 16-byte reads are free of
+// bank conflicts.  Per output the K loop runs in order: the chain is exactly the contract's.
+template <typename XT>
+__global__ __launch_bounds__(256) void router_logits_many_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
+                                                                 const float* __restrict__ bias, float* __restrict__ L,
+                                                                 int T, int d, int E, int vec)
 {
-    constexpr int TX = BE / RE, TY = BT / RT;
-    static_assert(TX * TY == 256, "256 threads");
-    __shared__ float xs[BK][BT];
-    __shared__ float wsm[BK][BE];
-    const int tid = threadIdx.x, tx = tid % TX, ty = tid / TX;
+    constexpr int BT = 64, BE = 64, BK = 32;
+    __shared__ __attribute__((aligned(16))) float xs[2][BK][BT];
+    __shared__ __attribute__((aligned(16))) float wsm[2][BK][BE];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int e0 = blockIdx.x * BE, t0 = blockIdx.y * BT;
-
-    float acc[RT][RE];
+    // loader roles: x -> token (tid & 63), 8 consecutive i at (tid >> 6) * 8; Wg -> rows tid / 16 and
+    // tid / 16 + 16, 4 experts at (tid & 15) * 4
+    const int lx_t = tid & 63, lx_k = (tid >> 6) * 8;
+    const int lw_k = tid >> 4, lw_c = (tid & 15) * 4;
+    float xr[8];
+    float4 wr[2];
+    auto load = [&](int k0) {
+        if (t0 + lx_t < T) {
+            ldx8(x + (size_t)(t0 + lx_t) * d + k0 + lx_k, xr);
+        } else {
 #pragma unroll
-    for (int r = 0; r < RT; r++)
+            for (int j = 0; j < 8; j++) xr[j] = 0.f;
+        }
 #pragma unroll
-        for (int c = 0; c < RE; c++) acc[r][c] = 0.0f;
+        for (int h = 0; h < 2; h++) {
+            const float* row = Wg + (size_t)(k0 + lw_k + 16 * h) * E + e0 + lw_c;
+            if (vec && e0 + lw_c + 4 <= E) {
+                wr[h] = *(const float4*)row;
+            } else {
+                wr[h].x = e0 + lw_c + 0 < E ? row[0] : 0.f;
+                wr[h].y = e0 + lw_c + 1 < E ? row[1] : 0.f;
+                wr[h].z = e0 + lw_c + 2 < E ? row[2] : 0.f;
+                wr[h].w = e0 + lw_c + 3 < E ? row[3] : 0.f;
+            }
+        }
+    };
+    auto store = [&](int b) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) xs[b][lx_k + j][lx_t] = xr[j];
+#pragma unroll
+        for (int h = 0; h < 2; h++) *(float4*)&wsm[b][lw_k + 16 * h][lw_c] = wr[h];
+    };
 
-    for (int k0 = 0; k0 < d; k0 += BK) {
-        for (int f = tid; f < BT * BK; f += 256) {           // x tile, stored transposed
-            const int t = f / BK, kk = f % BK;
-            xs[kk][t] = (t0 + t < T) ? ldx<XT>(x + (size_t)(t0 + t) * d + k0 + kk) : 0.0f;
-        }
-        for (int f = tid; f < BK * BE; f += 256) {           // Wg tile, rows of BE experts
-            const int kk = f / BE, c = f % BE;
-            wsm[kk][c] = (e0 + c < E) ? Wg[(size_t)(k0 + kk) * E + e0 + c] : 0.0f;
-        }
-        __syncthreads();
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) acc[r][c] = 0.0f;
+
+    const int ns = d / BK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < ns; s++) {
+        const int b = s & 1;
+        if (s + 1 < ns) load((s + 1) * BK);
 #pragma unroll 8
         for (int kk = 0; kk < BK; kk++) {
-            float a[RT], b[RE];
+            const float4 a = *(const float4*)&xs[b][kk][ty * 4];
+            const float4 w = *(const float4*)&wsm[b][kk][tx * 4];
+            const float av[4] = {a.x, a.y, a.z, a.w}, wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int r = 0; r < RT; r++) a[r] = xs[kk][ty * RT + r];
+            for (int r = 0; r < 4; r++)
 #pragma unroll
-            for (int c = 0; c < RE; c++) b[c] = wsm[kk][tx * RE + c];
-#pragma unroll
-            for (int r = 0; r < RT; r++)
-#pragma unroll
-                for (int c = 0; c < RE; c++) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
+                for (int c = 0; c < 4; c++) acc[r][c] = __builtin_fmaf(av[r], wv[c], acc[r][c]);
         }
+        if (s + 1 < ns) store(b ^ 1);
         __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < RT; r++) {
-        const int t = t0 + ty * RT + r;
+    for (int r = 0; r < 4; r++) {
+        const int t = t0 + ty * 4 + r;
         if (t >= T) continue;
 #pragma unroll
-        for (int c = 0; c < RE; c++) {
-            const int e = e0 + tx * RE + c;
+        for (int c = 0; c < 4; c++) {
+            const int e = e0 + tx * 4 + c;
             if (e >= E) continue;
             float v = acc[r][c];
             if (bias) v = v + bias[e];
@@ -204,11 +234,12 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
         else
             router_logits_few_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E, vec);
     } else {
+        const int vec = (E % 4 == 0) && (((uintptr_t)Wg & 15) == 0);
         dim3 grid((E + 63) / 64, (T + 63) / 64);
         if (bf)
-            router_logits_kernel<uint16_t, 64, 64, 4, 4, 32><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E, vec);
         else
-            router_logits_kernel<float, 64, 64, 4, 4, 32><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E, vec);
     }
     return hipGetLastError();
 }
