@@ -54,7 +54,8 @@ struct GemmArgs {
     int K_r, K_s;             // reduction length: routed / shared
     int n_blocks;             // n-blocks per tile (over the larger N)
     int max_tiles;
-    int tile_major;           // 1: consecutive blocks walk tiles (weight reuse); 0: walk n-blocks
+    int group_m;              // 0: block b -> (tile b / n_blocks, n-block b % n_blocks); else the XCD-aware
+                              // grouped order below, with group_m tiles per group
 };
 
 template <int ET> struct Elem;
@@ -159,16 +160,19 @@ __device__ __forceinline__ void mma_stage(const uint8_t* As_lds, const uint8_t* 
 // stage but half the LDS, so two blocks share a CU and cover each other's barriers).  MINW: minimum
 // wavefronts per SIMD the register allocation must allow.
 template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, int MINW>
-__global__ __launch_bounds__(256, MINW) void grouped_gemm_kernel(GemmArgs g)
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_kernel(GemmArgs g)
 {
     constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
     constexpr int ROWS = BM + NB;                      // LDS rows per stage (128 bytes each)
     constexpr int CHUNKS = ROWS * 8;                   // 16-byte chunks per stage
-    constexpr int PER = (CHUNKS + 255) / 256;          // chunks per thread
+    constexpr int NT = 64 * WAVES_M * WAVES_N;         // threads per block
+    constexpr int PER = (CHUNKS + NT - 1) / NT;        // chunks per thread
     constexpr int WM = BM / 16 / WAVES_M, WN = BN / 16 / WAVES_N;
     constexpr int KE = 128 / Elem<ET>::bytes;          // K elements per stage
     constexpr bool FP8 = ET == ET_FP8;
-    static_assert(WAVES_M * WAVES_N == 4 && WM >= 1 && WN >= 1, "4 waves");
+    static_assert((WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8) && WM >= 1 && WN >= 1, "4 or 8 waves");
+    static_assert(BM <= NT, "one thread per tile row for the row tables");
+    static_assert(!FP8 || (WN * 16 <= 128 && 128 % (WN * 16) == 0), "a wavefront's columns share one fp8 block scale");
     static_assert(!(FP8 && UP) || BN % 128 == 0, "fp8 h quantisation needs whole 128-column groups");
 
     static_assert(!(FP8 && UP) || BM * BN * 4 <= NBUF * ROWS * 128, "h tile must fit the staging LDS");
@@ -176,12 +180,31 @@ __global__ __launch_bounds__(256, MINW) void grouped_gemm_kernel(GemmArgs g)
     __shared__ float sA[NBUF][BM];
     __shared__ int s_tok[BM];
 
-    // block -> (tile, n-block)
+    // block -> (tile, n-block).  Decode-sized tiles: consecutive blocks walk one tile's n-blocks.
+    // Otherwise blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8), so the
+    // work list (tile, n-block) is cut into 8 contiguous ranges, one per XCD, and inside a range the
+    // items go group by group: group_m consecutive tiles x all n-blocks, tiles fastest.  Blocks that run
+    // together on one XCD then share A rows (same tile) and weight panels (same expert, n-block) in
+    // that XCD's L2.
     const int bid = blockIdx.x;
     int tile, nb;
-    if (g.tile_major) { nb = bid / g.max_tiles; tile = bid % g.max_tiles; }
-    else { tile = bid / g.n_blocks; nb = bid % g.n_blocks; }
-    if (tile >= *g.ntiles) return;
+    if (g.group_m == 0) {
+        tile = bid / g.n_blocks;
+        nb = bid % g.n_blocks;
+        if (tile >= *g.ntiles) return;
+    } else {
+        const int nt = *g.ntiles;
+        const int total = nt * g.n_blocks;
+        const int per = (total + 7) / 8;
+        if (bid >= 8 * per) return;
+        const int l = (bid & 7) * per + (bid >> 3);
+        if (l >= total) return;
+        const int items = g.group_m * g.n_blocks;
+        const int c = l / items, r = l % items;
+        const int gm = min(g.group_m, nt - c * g.group_m);
+        nb = r / gm;
+        tile = c * g.group_m + r % gm;
+    }
     const int4 td = g.tiles[tile];
     const int grp = td.x, row0 = td.y, rows = td.z;
     const bool shared = grp == g.E;
@@ -195,8 +218,9 @@ __global__ __launch_bounds__(256, MINW) void grouped_gemm_kernel(GemmArgs g)
     const uint8_t* W1 = shared ? g.S1 : g.B1 + (int64_t)grp * N * ldb;
     const uint8_t* W3 = UP ? (shared ? g.S3 : g.B3 + (int64_t)grp * N * ldb) : nullptr;
     const int nkb = K / 128;                           // fp8 weight blocks along K
-    const float* W1s = FP8 ? (shared ? g.S1s : g.B1s + (int64_t)grp * (N / 128) * nkb) + (n0 / 128) * nkb : nullptr;
-    const float* W3s = (FP8 && UP) ? (shared ? g.S3s : g.B3s + (int64_t)grp * (N / 128) * nkb) + (n0 / 128) * nkb : nullptr;
+    // fp8: the block scales of this wavefront's output columns (its column span lies in one 128-block)
+    const float* W1s = FP8 ? (shared ? g.S1s : g.B1s + (int64_t)grp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
+    const float* W3s = (FP8 && UP) ? (shared ? g.S3s : g.B3s + (int64_t)grp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
 
     if (tid < BM) s_tok[tid] = tid < rows ? (UP ? g.row_token[row0 + tid] : row0 + tid) : -1;
     __syncthreads();
@@ -206,7 +230,7 @@ __global__ __launch_bounds__(256, MINW) void grouped_gemm_kernel(GemmArgs g)
     int dst[PER];
 #pragma unroll
     for (int p = 0; p < PER; p++) {
-        const int c = tid + p * 256;
+        const int c = tid + p * NT;
         src[p] = nullptr;
         dst[p] = -1;
         if (c < CHUNKS) {
@@ -291,7 +315,7 @@ __global__ __launch_bounds__(256, MINW) void grouped_gemm_kernel(GemmArgs g)
         __syncthreads();
         // 16 threads per (row, 128-column group), 8 columns each
         constexpr int GROUPS = BM * (BN / 128);
-        for (int gi = tid >> 4; gi < GROUPS; gi += 16) {
+        for (int gi = tid >> 4; gi < GROUPS; gi += NT / 16) {
             const int row = gi / (BN / 128), grp128 = gi % (BN / 128);
             const int sub = tid & 15;
             const float* v = hs + row * BN + grp128 * 128 + sub * 8;
@@ -373,8 +397,9 @@ hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace
 template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N, int NBUF = 2, int MINW = 1>
 static void launch_one(GemmArgs a, hipStream_t stream)
 {
-    const int64_t nblk = (int64_t)a.n_blocks * a.max_tiles;
-    grouped_gemm_kernel<ET, UP, ACT_BF16, BM, BN, WAVES_M, WAVES_N, NBUF, MINW><<<(unsigned)nblk, 256, 0, stream>>>(a);
+    const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
+    grouped_gemm_kernel<ET, UP, ACT_BF16, BM, BN, WAVES_M, WAVES_N, NBUF, MINW>
+        <<<(unsigned)nblk, 64 * WAVES_M * WAVES_N, 0, stream>>>(a);
 }
 
 // Output features per block for the 128- and 256-row tile classes.
@@ -390,6 +415,33 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 #ifndef MOE_MID_MINW
 #define MOE_MID_MINW 2
 #endif
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 8
+#endif
+#ifndef MOE_FP8_WM
+#define MOE_FP8_WM 2
+#endif
+#ifndef MOE_FP8_WN
+#define MOE_FP8_WN 4
+#endif
+#ifndef MOE_FP8_NBUF
+#define MOE_FP8_NBUF 2
+#endif
+#ifndef MOE_FP8_MINW
+#define MOE_FP8_MINW 2
+#endif
+#ifndef MOE_FP8_DN_BN
+#define MOE_FP8_DN_BN 256
+#endif
+#ifndef MOE_BIG_WM
+#define MOE_BIG_WM 2
+#endif
+#ifndef MOE_BIG_WN
+#define MOE_BIG_WN 2
+#endif
+#ifndef MOE_BIG_MINW
+#define MOE_BIG_MINW 1
+#endif
 #ifndef MOE_BIG_DN_BN
 #define MOE_BIG_DN_BN 256
 #endif
@@ -402,7 +454,7 @@ static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws)
     a.ntiles = ws.sync;
     a.max_tiles = (int)ws.max_tiles;
     a.E = (int)s.E;
-    a.tile_major = tile_rows(s) > 16;
+    a.group_m = tile_rows(s) > 16 ? MOE_GROUP_M : 0;
     return a;
 }
 
@@ -437,7 +489,7 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     if (fp8) {
         up.n_blocks = (int)(ws.inter_max / 128);
         if (bm == 16) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
-        else launch_one<ET_FP8, true, true, 128, 128, 2, 2>(up, stream);
+        else launch_one<ET_FP8, true, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(up, stream);
     } else if (f32) {
         up.n_blocks = (int)(ws.inter_max / 64);
         if (bm == 16) launch_one<ET_F32, true, false, 16, 64, 1, 4>(up, stream);
@@ -451,7 +503,7 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
             launch_one<ET_BF16, true, true, 128, MOE_MID_UP_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(up, stream);
         } else {
             up.n_blocks = (int)(ws.inter_max / 128);
-            launch_one<ET_BF16, true, true, 256, 128, 2, 2>(up, stream);
+            launch_one<ET_BF16, true, true, 256, 128, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(up, stream);
         }
     }
     return hipGetLastError();
@@ -484,8 +536,8 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
         else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
     } else if (bm == 128) {
         if (fp8) {
-            dn.n_blocks = (int)(s.d / 128);
-            launch_one<ET_FP8, false, true, 128, 128, 2, 2>(dn, stream);
+            dn.n_blocks = (int)(s.d / MOE_FP8_DN_BN);
+            launch_one<ET_FP8, false, true, 128, MOE_FP8_DN_BN, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
         } else if (f32) {
             dn.n_blocks = (int)(s.d / 128);
             launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
@@ -495,7 +547,7 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
         }
     } else {
         dn.n_blocks = (int)(s.d / MOE_BIG_DN_BN);
-        launch_one<ET_BF16, false, true, 256, MOE_BIG_DN_BN, 2, 2>(dn, stream);
+        launch_one<ET_BF16, false, true, 256, MOE_BIG_DN_BN, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(dn, stream);
     }
     return hipGetLastError();
 }
