@@ -197,14 +197,25 @@ static void softmax_selected(const float* L, const int32_t* idx, int64_t k, floa
  *   pos[s]          inverse: the position of slot s in sorted_slots.
  * Any output pointer may be NULL except idx and w.
  */
-int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype, const void* x,
-                 const float* Wg, const float* bias, float* logits_out, int32_t* idx, float* w,
-                 int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos)
+static int route_impl(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype, const void* x,
+                      const float* Wg, const float* bias, const uint8_t* allowed, float* logits_out, int32_t* idx,
+                      float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos)
 {
     if (k < 1 || k > E || k > 64) return 1;
+    if (allowed) {   /* at least one allowed expert; with fewer than k, the rest come at -inf, weight 0 */
+        int64_t n_allowed = 0;
+        for (int64_t e = 0; e < E; e++) n_allowed += allowed[e] != 0;
+        if (n_allowed < 1) return 1;
+    }
     float* L = logits_out ? logits_out : (float*)malloc(sizeof(float) * (size_t)(T * E));
     if (!L) return 2;
     oracle_router_logits(T, d, E, act_dtype, x, Wg, bias, L);
+    /* Device-limited routing ["DeepSeek-V3's mixture-of-experts architecture explained", "Why 256
+     * experts with top-8 routing?", device_limited_routing]: a mask of -inf outside the allowed experts
+     * and 0 inside is added to the logits before top-k. */
+    if (allowed)
+        for (int64_t t = 0; t < T; t++)
+            for (int64_t e = 0; e < E; e++) L[t * E + e] = L[t * E + e] + (allowed[e] ? 0.0f : -INFINITY);
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; t++) {
         topk_one(L + t * E, E, k, idx + t * k);
@@ -235,6 +246,50 @@ int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype, cons
     return 0;
 }
 
+int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype, const void* x,
+                 const float* Wg, const float* bias, float* logits_out, int32_t* idx, float* w,
+                 int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos)
+{
+    return route_impl(T, d, E, k, act_dtype, x, Wg, bias, NULL, logits_out, idx, w, counts, offsets, sorted_slots,
+                      pos);
+}
+
+/* Routing restricted to the experts with allowed[e] != 0 (at least one of them). */
+int oracle_route_limited(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype, const void* x,
+                         const float* Wg, const float* bias, const uint8_t* allowed, float* logits_out,
+                         int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                         int32_t* pos)
+{
+    return route_impl(T, d, E, k, act_dtype, x, Wg, bias, allowed, logits_out, idx, w, counts, offsets,
+                      sorted_slots, pos);
+}
+
+/*
+ * Expert utilisation ["DeepSeek-V3's mixture-of-experts architecture explained", "Where the
+ * architecture struggles", log_expert_utilization]: utilization = counts.float() / counts.sum() (fp32
+ * division), with an alert for experts above 2x or below 0.1x the mean utilisation 1/E.  The alert
+ * thresholds are taken on the exact rationals: over <=> counts[e] * E > 2 * total,
+ * under <=> 10 * counts[e] * E < total.  flags[e] = +1 over, -1 under, 0 otherwise; summary = (#over,
+ * #under).
+ */
+int oracle_expert_utilization(int64_t E, const int32_t* counts, float* util, int32_t* flags, int32_t* summary)
+{
+    int64_t total = 0;
+    for (int64_t e = 0; e < E; e++) total += counts[e];
+    int32_t n_over = 0, n_under = 0;
+    for (int64_t e = 0; e < E; e++) {
+        util[e] = total > 0 ? (float)counts[e] / (float)total : 0.0f;
+        const int64_t c = counts[e];
+        const int over = total > 0 && c * E > 2 * total, under = total > 0 && 10 * c * E < total;
+        flags[e] = over ? 1 : under ? -1 : 0;
+        n_over += over;
+        n_under += under;
+    }
+    summary[0] = n_over;
+    summary[1] = n_under;
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------------------ */
 /* Experts [P5 "All 5 steps" and MLP forward].                                                         */
 /* ------------------------------------------------------------------------------------------------ */
@@ -244,11 +299,14 @@ typedef struct {
     int32_t act_dtype, w_dtype;
 } oracle_shape_t;
 
-/* One SwiGLU weight set: W1, W3 are [n_inter][d] and W2 is [d][n_inter] (nn.Linear [out][in]). */
+/* One SwiGLU weight set: W1, W3 are [.][d] and W2 is [d][ld2] (nn.Linear [out][in]).  The expert uses
+ * the n_inter hidden features starting at row0 of W1/W3 and column row0 of W2 (a tensor-parallel
+ * slice of a wider expert; row0 = 0 and ld2 = n_inter for a whole expert). */
 typedef struct {
     const void* w1; const void* w3; const void* w2;
     const float* s1; const float* s3; const float* s2;   /* fp8 block scales, else NULL */
     int64_t n_inter;
+    int64_t row0, ld2;
 } swiglu_weights_t;
 
 /* Values of all 256 E4M3 codes, filled from oracle_e4m3_decode before any parallel region. */
@@ -286,10 +344,11 @@ static void fp8_activation_view(const float* v, int64_t n, double* out)
     }
 }
 
-/* Row r of a [rows][cols] weight matrix as exact fp64 values. */
-static void weight_row(int w_dtype, const void* W, const float* S, int64_t cols, int64_t r, double* out)
+/* Columns [c0, c0 + n) of row r of a [rows][cols] weight matrix as exact fp64 values. */
+static void weight_row(int w_dtype, const void* W, const float* S, int64_t cols, int64_t r, int64_t c0, int64_t n,
+                       double* out)
 {
-    for (int64_t c = 0; c < cols; c++) out[c] = weight_value(w_dtype, W, S, cols, r, c);
+    for (int64_t c = 0; c < n; c++) out[c] = weight_value(w_dtype, W, S, cols, r, c0 + c);
 }
 
 static double dot(const double* a, const double* b, int64_t n)
@@ -314,8 +373,8 @@ static void swiglu_row(const oracle_shape_t* sh, const swiglu_weights_t* W, cons
     else for (int64_t i = 0; i < d; i++) xin[i] = xv[i];
 
     for (int64_t n = 0; n < n_inter; n++) {
-        weight_row(sh->w_dtype, W->w1, W->s1, d, n, row1);
-        weight_row(sh->w_dtype, W->w3, W->s3, d, n, row3);
+        weight_row(sh->w_dtype, W->w1, W->s1, d, W->row0 + n, 0, d, row1);
+        weight_row(sh->w_dtype, W->w3, W->s3, d, W->row0 + n, 0, d, row3);
         float g = round_act(sh->act_dtype, dot(xin, row1, d));      /* g = x W1 */
         float u = round_act(sh->act_dtype, dot(xin, row3, d));      /* u = x W3 */
         float sig = 1.0f / (1.0f + expf(-g));                        /* sigma(g), fp32 */
@@ -327,7 +386,7 @@ static void swiglu_row(const oracle_shape_t* sh, const swiglu_weights_t* W, cons
     else for (int64_t n = 0; n < n_inter; n++) hin[n] = h[n];
 
     for (int64_t m = 0; m < d; m++) {                                /* y = h W2 */
-        weight_row(sh->w_dtype, W->w2, W->s2, n_inter, m, row1);
+        weight_row(sh->w_dtype, W->w2, W->s2, W->ld2, m, W->row0, n_inter, row1);
         y_out[m] = round_act(sh->act_dtype, dot(hin, row1, n_inter));
     }
     free(xin); free(row1); free(row3); free(h); free(hin);
@@ -380,7 +439,7 @@ int oracle_forward(const oracle_shape_t* sh, const void* x,
                 fp8 ? W1s + e * nb_mid * nb_in : NULL,
                 fp8 ? W3s + e * nb_mid * nb_in : NULL,
                 fp8 ? W2s + e * nb_in * nb_mid : NULL,
-                inter};
+                inter, 0, inter};
             swiglu_row(sh, &we, xv, ye);
             const float wj = w[t * k + j];
             for (int64_t m = 0; m < d; m++) {
@@ -388,7 +447,7 @@ int oracle_forward(const oracle_shape_t* sh, const void* x,
                 acc[m] = acc[m] + p;
             }
         }
-        swiglu_weights_t ws = {S1, S3, S2, S1s, S3s, S2s, sh->inter_shared};
+        swiglu_weights_t ws = {S1, S3, S2, S1s, S3s, S2s, sh->inter_shared, 0, sh->inter_shared};
         swiglu_row(sh, &ws, xv, ye);
         for (int64_t m = 0; m < d; m++) acc[m] = acc[m] + ye[m];
 
@@ -401,12 +460,75 @@ int oracle_forward(const oracle_shape_t* sh, const void* x,
     return 0;
 }
 
+/*
+ * One expert-parallel rank's share of the layer [P5 MoE __init__/forward: the rank owns experts
+ * [experts_start_idx, experts_end_idx) and a slice of the shared expert built with
+ * reduce_output=False; the fp32 partial y is what dist.all_reduce(y) sums over ranks]:
+ *   partial[t] = sum over the token's experts e in [e0, e1), ascending, of float(expert_e(x[t]) * w)
+ *              + (if s0 < s1) the shared expert's hidden features [s0, s1): its W2 partial product
+ *                rounded to the activation dtype, as a row-parallel linear returns it;
+ * no final rounding.  With e0 = 0, e1 = E, s0 = 0, s1 = inter_shared this is oracle_forward's fp32 out.
+ */
+int oracle_forward_shard(const oracle_shape_t* sh, const void* x,
+                         const void* W1, const void* W3, const void* W2,
+                         const float* W1s, const float* W3s, const float* W2s,
+                         const void* S1, const void* S3, const void* S2,
+                         const float* S1s, const float* S3s, const float* S2s,
+                         const int32_t* idx, const float* w, int64_t e0, int64_t e1, int64_t s0, int64_t s1,
+                         int64_t n_tok, const int32_t* tokens, float* partial)
+{
+    const int64_t d = sh->d, E = sh->E, k = sh->k, inter = sh->inter, is = sh->inter_shared;
+    const int fp8 = sh->w_dtype == ORACLE_FP8_E4M3;
+    if (fp8 && (d % 128 || inter % 128 || is % 128 || s0 % 128 || s1 % 128)) return 1;
+    if (!fp8 && sh->w_dtype != sh->act_dtype) return 1;
+    if (e0 < 0 || e1 > E || e0 > e1 || s0 < 0 || s1 > is || s0 > s1) return 1;
+    const size_t eb = w_elem_bytes(sh->w_dtype);
+    const int64_t nb_in = d / 128, nb_mid = inter / 128;
+    fill_e4m3_values();
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_tok; r++) {
+        const int64_t t = tokens[r];
+        float* xv = (float*)malloc(sizeof(float) * (size_t)d);
+        float* ye = (float*)malloc(sizeof(float) * (size_t)d);
+        float* acc = partial + r * d;
+        for (int64_t i = 0; i < d; i++) xv[i] = act_value(sh->act_dtype, x, t * d + i);
+        for (int64_t m = 0; m < d; m++) acc[m] = 0.0f;
+        for (int64_t e = e0; e < e1; e++) {
+            int64_t j = -1;
+            for (int64_t jj = 0; jj < k; jj++) if (idx[t * k + jj] == e) j = jj;
+            if (j < 0) continue;
+            swiglu_weights_t we = {
+                (const char*)W1 + (size_t)e * inter * d * eb,
+                (const char*)W3 + (size_t)e * inter * d * eb,
+                (const char*)W2 + (size_t)e * d * inter * eb,
+                fp8 ? W1s + e * nb_mid * nb_in : NULL,
+                fp8 ? W3s + e * nb_mid * nb_in : NULL,
+                fp8 ? W2s + e * nb_in * nb_mid : NULL,
+                inter, 0, inter};
+            swiglu_row(sh, &we, xv, ye);
+            const float wj = w[t * k + j];
+            for (int64_t m = 0; m < d; m++) {
+                float p = ye[m] * wj;
+                acc[m] = acc[m] + p;
+            }
+        }
+        if (s0 < s1) {
+            swiglu_weights_t ws = {S1, S3, S2, S1s, S3s, S2s, s1 - s0, s0, is};
+            swiglu_row(sh, &ws, xv, ye);
+            for (int64_t m = 0; m < d; m++) acc[m] = acc[m] + ye[m];
+        }
+        free(xv); free(ye);
+    }
+    return 0;
+}
+
 /* One SwiGLU expert applied to rows of activations, exposed for the dense-reduction check. */
 int oracle_swiglu_rows(const oracle_shape_t* sh, const void* w1, const void* w3, const void* w2,
                        const float* s1, const float* s3, const float* s2, int64_t n_inter,
                        int64_t rows, const float* xv, float* y)
 {
-    swiglu_weights_t W = {w1, w3, w2, s1, s3, s2, n_inter};
+    swiglu_weights_t W = {w1, w3, w2, s1, s3, s2, n_inter, 0, n_inter};
     fill_e4m3_values();
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < rows; r++) swiglu_row(sh, &W, xv + r * sh->d, y + r * sh->d);

@@ -40,6 +40,9 @@ def lib():
         L.oracle_route.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [ctypes.POINTER(OracleShape)] + [vp] * 15 + [i64, vp, vp, vp]
         L.oracle_swiglu_rows.argtypes = [ctypes.POINTER(OracleShape)] + [vp] * 6 + [i64, i64, vp, vp]
+        L.oracle_route_limited.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_expert_utilization.argtypes = [i64, vp, vp, vp, vp]
+        L.oracle_forward_shard.argtypes = [ctypes.POINTER(OracleShape)] + [vp] * 15 + [i64, i64, i64, i64, i64, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -105,6 +108,53 @@ def route(x: np.ndarray, Wg: np.ndarray, bias, k: int, act_dtype: int) -> dict:
     if rc:
         raise ValueError(f"oracle_route failed ({rc})")
     return out
+
+
+def route_limited(x: np.ndarray, Wg: np.ndarray, bias, allowed: np.ndarray, k: int, act_dtype: int) -> dict:
+    """route() with the logits of experts where allowed[e] == 0 set to -inf before top-k."""
+    x = np.ascontiguousarray(x)
+    Wg = np.ascontiguousarray(Wg, dtype=np.float32)
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    allowed = np.ascontiguousarray(allowed, dtype=np.uint8)
+    T, d = x.shape
+    E = Wg.shape[1]
+    out = dict(logits=np.empty((T, E), np.float32), idx=np.empty((T, k), np.int32),
+               w=np.empty((T, k), np.float32), counts=np.empty(E, np.int32),
+               offsets=np.empty(E + 1, np.int32), sorted_slots=np.empty(T * k, np.int32),
+               pos=np.empty(T * k, np.int32))
+    rc = lib().oracle_route_limited(T, d, E, k, act_dtype, _p(x), _p(Wg), _p(bias), _p(allowed), _p(out["logits"]),
+                                    _p(out["idx"]), _p(out["w"]), _p(out["counts"]), _p(out["offsets"]),
+                                    _p(out["sorted_slots"]), _p(out["pos"]))
+    if rc:
+        raise ValueError(f"oracle_route_limited failed ({rc})")
+    return out
+
+
+def expert_utilization(counts: np.ndarray):
+    """(utilization fp32 [E], flags int32 [E] (+1 over 2x mean, -1 under 0.1x mean), (n_over, n_under))."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    E = counts.shape[0]
+    util = np.empty(E, np.float32)
+    flags = np.empty(E, np.int32)
+    summary = np.empty(2, np.int32)
+    lib().oracle_expert_utilization(E, _p(counts), _p(util), _p(flags), _p(summary))
+    return util, flags, (int(summary[0]), int(summary[1]))
+
+
+def forward_shard(shape: dict, x, W1, W3, W2, S1, S3, S2, idx, w, e0, e1, s0, s1, tokens=None,
+                  W1s=None, W3s=None, W2s=None, S1s=None, S3s=None, S2s=None):
+    """fp32 partial output of one expert-parallel rank: experts [e0, e1) + shared features [s0, s1)."""
+    sh = OracleShape(**shape)
+    T, d = int(shape["T"]), int(shape["d"])
+    toks = np.arange(T, dtype=np.int32) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    n = toks.shape[0]
+    part = np.empty((n, d), np.float32)
+    args = [np.ascontiguousarray(a) if a is not None else None
+            for a in (x, W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s, S2s, idx, w)]
+    rc = lib().oracle_forward_shard(ctypes.byref(sh), *[_p(a) for a in args], e0, e1, s0, s1, n, _p(toks), _p(part))
+    if rc:
+        raise ValueError(f"oracle_forward_shard failed ({rc})")
+    return part
 
 
 def forward(shape: dict, x, W1, W3, W2, S1, S3, S2, idx, w, tokens=None,
