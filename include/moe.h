@@ -138,6 +138,69 @@ moe_status_t moe_forward_staged(const moe_shape_t* shape, const void* x, const f
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* events);
 
+/*
+ * Device-limited routing ("DeepSeek-V3's mixture-of-experts architecture explained", "Why 256 experts
+ * with top-8 routing?", device_limited_routing: logits outside the experts of the current device get a
+ * -inf mask before the top-k).  moe_route with one extra input:
+ *   allowed  [E] uint8 device array, nonzero = the expert may be selected; the same mask for every
+ *            token.  Required (NULL -> MOE_ERR_INVALID_ARG).
+ * Selection is the top-k of (logit + mask) with the mask -inf outside `allowed` and 0 inside, equal
+ * values -> lower expert index; the softmax is over those k masked values.  When fewer than k experts
+ * are allowed, the surplus slots select the lowest-index experts outside `allowed` and get weight 0.
+ * At least one entry of `allowed` must be nonzero (it lives in device memory, so this is not
+ * checked); with none, every weight is NaN.  All other arguments, outputs and guarantees as moe_route.
+ */
+moe_status_t moe_route_limited(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                               const uint8_t* allowed, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * One expert-parallel rank's share of the layer ("DeepSeek-V3.2-Exp / Mixture of experts", MoE
+ * __init__ and forward excerpts: a rank owns the routed experts [experts_start_idx, experts_end_idx)
+ * and a slice of the shared expert, adds their outputs into an fp32 y, and dist.all_reduce(y) sums the
+ * ranks' y).  Every token is routed over all E experts (or the `allowed` ones), as each rank runs the
+ * full gate; only the rank's experts and shared slice are computed.
+ *   allowed   [E] uint8 routing mask as in moe_route_limited, or NULL for plain routing
+ *   e0, e1    routed experts of this rank, 0 <= e0 <= e1 <= E (e0 == e1: none)
+ *   n_shared  shared-expert hidden features of this rank, 0 <= n_shared <= inter_shared, multiple of 128
+ *   W1, W3    [e1 - e0, inter, d] w_dtype, W2 [e1 - e0, d, inter]: the rank's experts only (expert e
+ *             at index e - e0); scales W1s, W3s, W2s likewise.  May be NULL when e0 == e1.
+ *   S1, S3    [n_shared, d] w_dtype, S2 [d, n_shared]: the rank's slice of the shared expert (rows of
+ *             S1/S3 and the matching columns of S2, stored densely); scales S1s, S3s
+ *             [n_shared/128, d/128], S2s [d/128, n_shared/128].  May be NULL when n_shared == 0.
+ *   y_partial out [T, d] fp32:  sum over the token's selected experts e in [e0, e1), ascending e, of
+ *             w * expert_e(x) (each expert output rounded to act_dtype, the products summed in fp32),
+ *             then + the shared slice's output (its W2 product rounded to act_dtype).  Not rounded.
+ *   idx_out, w_out, counts_out  optional copies of the full routing, as in moe_forward.
+ * With e0 = 0, e1 = E, n_shared = inter_shared, rounding y_partial to act_dtype gives moe_forward's y
+ * bitwise.  The sum of y_partial over ranks that partition the experts and the shared features is the
+ * layer output up to fp32 reassociation and the rounding of each shared slice.
+ * shape->inter_shared is the full shared width (it sizes the workspace; moe_workspace_size applies).
+ */
+moe_status_t moe_forward_shard(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                               const uint8_t* allowed, int64_t e0, int64_t e1, int64_t n_shared,
+                               const void* W1, const void* W3, const void* W2,
+                               const float* W1s, const float* W3s, const float* W2s,
+                               const void* S1, const void* S3, const void* S2,
+                               const float* S1s, const float* S3s, const float* S2s,
+                               float* y_partial, int32_t* idx_out, float* w_out, int32_t* counts_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Expert-utilisation monitor ("DeepSeek-V3's mixture-of-experts architecture explained", "Where the
+ * architecture struggles", log_expert_utilization: utilisation = bincount / its sum, with an alert for
+ * experts above 2x or below 0.1x the mean).  One single-block launch.
+ *   counts      [E] int32 device: tokens per expert (the counts output of moe_route / moe_forward)
+ *   util   out  [E] fp32: float(counts[e]) / float(sum of counts), correctly rounded; 0 if the sum is 0
+ *   flags  out  [E] int32: +1 if util > 2/E, -1 if util < 0.1/E, else 0, decided exactly on the
+ *               integers (counts[e] * E > 2 * sum, 10 * counts[e] * E < sum); all 0 if the sum is 0
+ *   summary out [2] int32: number of +1 flags, number of -1 flags
+ * E >= 1 (else MOE_ERR_INVALID_ARG); counts must be >= 0.
+ */
+moe_status_t moe_expert_utilization(int64_t E, const int32_t* counts, float* util, int32_t* flags,
+                                    int32_t* summary, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t status);
 

@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_staged", "moe_status_string")
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_staged", "moe_route_limited",
+           "moe_forward_shard", "moe_expert_utilization", "moe_status_string")
 NUM_STAGES = 7
 STAGE_NAMES = ("router_logits", "topk_softmax", "permute", "x_quant", "up_gemm", "down_gemm", "combine")
 
@@ -49,6 +50,13 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [sp] + [vp] * 20 + [ctypes.c_size_t, vp]
         L.moe_forward_staged.restype = ctypes.c_int
         L.moe_forward_staged.argtypes = [sp] + [vp] * 20 + [ctypes.c_size_t, vp, vp]
+        L.moe_route_limited.restype = ctypes.c_int
+        L.moe_route_limited.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp]
+        i64 = ctypes.c_int64
+        L.moe_forward_shard.restype = ctypes.c_int
+        L.moe_forward_shard.argtypes = [sp] + [vp] * 4 + [i64] * 3 + [vp] * 17 + [ctypes.c_size_t, vp]
+        L.moe_expert_utilization.restype = ctypes.c_int
+        L.moe_expert_utilization.argtypes = [i64] + [vp] * 5
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         _LIB = L
@@ -93,8 +101,10 @@ def _workspace(shape, dev, workspace):
     return workspace, need
 
 
-def moe_route(x, Wg, bias, k, workspace=None):
-    """Routing of x [T, d]: returns dict(idx, w, counts, offsets, sorted_slots, pos) as device tensors."""
+def moe_route(x, Wg, bias, k, workspace=None, allowed=None):
+    """Routing of x [T, d]: returns dict(idx, w, counts, offsets, sorted_slots, pos) as device tensors.
+
+    With `allowed` (uint8 [E] device tensor) calls moe_route_limited (device-limited routing)."""
     T, d = x.shape
     E = Wg.shape[1]
     shape = make_shape(T, d, E, k, 128, 128, _act_code(x), _act_code(x))
@@ -104,12 +114,26 @@ def moe_route(x, Wg, bias, k, workspace=None):
     out = dict(idx=torch.empty((T, k), **i32), w=torch.empty((T, k), dtype=torch.float32, device=dev),
                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
                sorted_slots=torch.empty(T * k, **i32), pos=torch.empty(T * k, **i32))
-    st = lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(out["idx"]), _ptr(out["w"]),
-                         _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["sorted_slots"]), _ptr(out["pos"]),
-                         _ptr(workspace), workspace.numel(), _stream(dev))
+    tail = [_ptr(out["idx"]), _ptr(out["w"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+            _ptr(out["sorted_slots"]), _ptr(out["pos"]), _ptr(workspace), workspace.numel(), _stream(dev)]
+    if allowed is not None:
+        _check_allowed(allowed, E)
+        st = lib().moe_route_limited(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(allowed), *tail)
+    else:
+        st = lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), *tail)
     if st:
-        raise MoeError(st, "moe_route")
+        raise MoeError(st, "moe_route_limited" if allowed is not None else "moe_route")
     return out
+
+
+def moe_route_limited(x, Wg, bias, allowed, k, workspace=None):
+    """Device-limited routing: moe_route with the per-expert mask `allowed` (uint8 [E] device tensor)."""
+    return moe_route(x, Wg, bias, k, workspace=workspace, allowed=allowed)
+
+
+def _check_allowed(allowed, E):
+    if allowed.dtype != torch.uint8 or allowed.numel() != E or not allowed.is_contiguous():
+        raise ValueError("allowed must be a contiguous uint8 tensor of E entries")
 
 
 def moe_forward(x, Wg, bias, W1, W3, W2, S1, S3, S2, k, scales=None, y=None, workspace=None, routing=False,
@@ -152,3 +176,80 @@ def forward_inputs(inp: dict, k: int, **kw):
     scales = {n: inp[n] for n in ("W1s", "W3s", "W2s", "S1s", "S3s", "S2s") if inp.get(n) is not None}
     return moe_forward(inp["x"], inp["Wg"], inp.get("bias"), inp["W1"], inp["W3"], inp["W2"], inp["S1"], inp["S3"],
                        inp["S2"], k, scales=scales or None, **kw)
+
+
+def moe_forward_shard(x, Wg, bias, k, e0, e1, W1, W3, W2, S1, S3, S2, inter, inter_shared, allowed=None,
+                      scales=None, y_partial=None, workspace=None, routing=False):
+    """One expert-parallel rank's fp32 partial output [T, d] (moe_forward_shard).
+
+    W1, W3 [e1-e0, inter, d], W2 [e1-e0, d, inter]: the rank's experts (None when e0 == e1);
+    S1, S3 [n_shared, d], S2 [d, n_shared]: its shared slice (None for none); `inter`, `inter_shared`:
+    the layer's full widths.  With routing=True returns (y_partial, dict(idx, w, counts)).
+    """
+    T, d = x.shape
+    E = Wg.shape[1]
+    n_shared = 0 if S1 is None else S1.shape[0]
+    wt = W1 if W1 is not None else S1
+    shape = make_shape(T, d, E, k, inter, inter_shared, _act_code(x), _w_code(wt) if wt is not None else _act_code(x))
+    dev = x.device
+    workspace, need = _workspace(shape, dev, workspace)
+    if y_partial is None:
+        y_partial = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if allowed is not None:
+        _check_allowed(allowed, E)
+    sc = scales or {}
+    r = None
+    if routing:
+        r = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+                 w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                 counts=torch.empty(E, dtype=torch.int32, device=dev))
+    st = lib().moe_forward_shard(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(allowed), e0, e1, n_shared,
+                                 _ptr(W1), _ptr(W3), _ptr(W2), _ptr(sc.get("W1s")), _ptr(sc.get("W3s")),
+                                 _ptr(sc.get("W2s")), _ptr(S1), _ptr(S3), _ptr(S2), _ptr(sc.get("S1s")),
+                                 _ptr(sc.get("S3s")), _ptr(sc.get("S2s")), _ptr(y_partial),
+                                 _ptr(r and r["idx"]), _ptr(r and r["w"]), _ptr(r and r["counts"]),
+                                 _ptr(workspace), workspace.numel(), _stream(dev))
+    if st:
+        raise MoeError(st, "moe_forward_shard")
+    return (y_partial, r) if routing else y_partial
+
+
+def shard_weights(inp: dict, e0: int, e1: int, s0: int, s1: int) -> dict:
+    """The rank-local weight arrays of experts [e0, e1) and shared features [s0, s1) of a full-layer dict
+    (as workloads.generate makes), stored densely as moe_forward_shard expects."""
+    fp8 = inp.get("W1s") is not None
+    out = {}
+    if e1 > e0:
+        for n in ("W1", "W3", "W2") + (("W1s", "W3s", "W2s") if fp8 else ()):
+            out[n] = inp[n][e0:e1].contiguous()
+    if s1 > s0:
+        out["S1"] = inp["S1"][s0:s1].contiguous()
+        out["S3"] = inp["S3"][s0:s1].contiguous()
+        out["S2"] = inp["S2"][:, s0:s1].contiguous()
+        if fp8:
+            out["S1s"] = inp["S1s"][s0 // 128:s1 // 128].contiguous()
+            out["S3s"] = inp["S3s"][s0 // 128:s1 // 128].contiguous()
+            out["S2s"] = inp["S2s"][:, s0 // 128:s1 // 128].contiguous()
+    return out
+
+
+def shard_inputs(inp: dict, k: int, e0: int, e1: int, s0: int, s1: int, **kw):
+    """moe_forward_shard over a workloads.generate dict: slices the rank's weights, then calls it."""
+    lw = shard_weights(inp, e0, e1, s0, s1)
+    scales = {n: lw[n] for n in ("W1s", "W3s", "W2s", "S1s", "S3s", "S2s") if n in lw}
+    return moe_forward_shard(inp["x"], inp["Wg"], inp.get("bias"), k, e0, e1, lw.get("W1"), lw.get("W3"),
+                             lw.get("W2"), lw.get("S1"), lw.get("S3"), lw.get("S2"), inp["W1"].shape[1],
+                             inp["S1"].shape[0], scales=scales or None, **kw)
+
+
+def moe_expert_utilization(counts):
+    """(util fp32 [E], flags int32 [E], summary int32 [2]) of an int32 [E] device tensor of counts."""
+    E = counts.numel()
+    dev = counts.device
+    util = torch.empty(E, dtype=torch.float32, device=dev)
+    flags = torch.empty(E, dtype=torch.int32, device=dev)
+    summary = torch.empty(2, dtype=torch.int32, device=dev)
+    st = lib().moe_expert_utilization(E, _ptr(counts), _ptr(util), _ptr(flags), _ptr(summary), _stream(dev))
+    if st:
+        raise MoeError(st, "moe_expert_utilization")
+    return util, flags, summary

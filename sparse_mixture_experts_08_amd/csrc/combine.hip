@@ -83,4 +83,127 @@ hipError_t launch_combine(const moe_shape_t& s, const int32_t* pos, const float*
     return hipGetLastError();
 }
 
+// One expert-parallel rank's partial output ("DeepSeek-V3.2-Exp / Mixture of experts", MoE forward: the
+// rank adds its local experts' weighted outputs and its shared-expert slice into an fp32 y that
+// dist.all_reduce(y) then sums over ranks).  Same fixed order as combine_kernel, restricted to the slots
+// whose expert lies in [e0, e1), plus the shared row when with_shared; stored in fp32 without rounding.
+template <bool ACT_BF16>
+__global__ __launch_bounds__(256) void combine_partial_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ pos,
+                                                              const float* __restrict__ w, const uint8_t* __restrict__ y_rows,
+                                                              int T, int d, int k, int e0, int e1, int with_shared,
+                                                              float* __restrict__ out)
+{
+    constexpr int EB = ACT_BF16 ? 2 : 4;
+    constexpr int VE = 16 / EB;
+    const int t = blockIdx.x;
+    int rr[16];
+    float ww[16];
+    int n = 0;
+    for (int j = 0; j < k; j++) {
+        const int e = idx[(size_t)t * k + j];
+        if (e < e0 || e >= e1) continue;
+        rr[n] = pos[(size_t)t * k + j];
+        ww[n] = w[(size_t)t * k + j];
+        n++;
+    }
+    for (int a = 1; a < n; a++) {                 // ascending row order = ascending expert
+        const int r = rr[a];
+        const float v = ww[a];
+        int b = a - 1;
+        while (b >= 0 && rr[b] > r) {
+            rr[b + 1] = rr[b];
+            ww[b + 1] = ww[b];
+            b--;
+        }
+        rr[b + 1] = r;
+        ww[b + 1] = v;
+    }
+    const int64_t shared_row = (int64_t)T * k + t;
+    for (int c = threadIdx.x * VE; c < d; c += 256 * VE) {
+        float acc[VE];
+#pragma unroll
+        for (int e = 0; e < VE; e++) acc[e] = 0.0f;
+        for (int j = 0; j < n; j++) {
+            const uint4 raw = *(const uint4*)(y_rows + ((int64_t)rr[j] * d + c) * EB);
+            const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < VE; e++) {
+                float v;
+                if constexpr (ACT_BF16) v = __uint_as_float(e & 1 ? (wv[e / 2] & 0xFFFF0000u) : (wv[e / 2] << 16));
+                else v = __uint_as_float(wv[e]);
+                acc[e] = acc[e] + v * ww[j];
+            }
+        }
+        if (with_shared) {
+            const uint4 raw = *(const uint4*)(y_rows + (shared_row * d + c) * EB);
+            const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < VE; e++) {
+                float v;
+                if constexpr (ACT_BF16) v = __uint_as_float(e & 1 ? (wv[e / 2] & 0xFFFF0000u) : (wv[e / 2] << 16));
+                else v = __uint_as_float(wv[e]);
+                acc[e] = acc[e] + v;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VE; e += 4)
+            *(float4*)(out + (int64_t)t * d + c + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+}
+
+hipError_t launch_combine_partial(const moe_shape_t& s, const int32_t* idx, const int32_t* pos, const float* w,
+                                  const Workspace& ws, int e0, int e1, int with_shared, float* y_partial,
+                                  hipStream_t stream)
+{
+    if (s.act_dtype == MOE_BF16)
+        combine_partial_kernel<true><<<(unsigned)s.T, 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
+                                                                        (int)s.d, (int)s.k, e0, e1, with_shared, y_partial);
+    else
+        combine_partial_kernel<false><<<(unsigned)s.T, 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
+                                                                         (int)s.d, (int)s.k, e0, e1, with_shared, y_partial);
+    return hipGetLastError();
+}
+
+// Expert utilisation ("DeepSeek-V3's mixture-of-experts architecture explained", "Where the
+// architecture struggles", log_expert_utilization): utilisation = counts / sum(counts) in fp32, and an
+// alert flag per expert above 2x or below 0.1x the mean utilisation 1/E, decided on the exact integers
+// (counts[e] * E > 2 * total, 10 * counts[e] * E < total).  One block; summary = (#over, #under).
+__global__ __launch_bounds__(1024) void expert_utilization_kernel(int E, const int32_t* __restrict__ counts,
+                                                                  float* __restrict__ util, int32_t* __restrict__ flags,
+                                                                  int32_t* __restrict__ summary)
+{
+    __shared__ long long tot_lds[16];
+    __shared__ int n_over, n_under;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    long long part = 0;
+    for (int e = tid; e < E; e += 1024) part += counts[e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    if (lane == 0) tot_lds[wave] = part;
+    if (tid == 0) n_over = n_under = 0;
+    __syncthreads();
+    long long total = 0;
+    for (int i = 0; i < 16; i++) total += tot_lds[i];
+    for (int e = tid; e < E; e += 1024) {
+        const long long c = counts[e];
+        util[e] = total > 0 ? (float)c / (float)total : 0.0f;
+        const int over = total > 0 && c * E > 2 * total, under = total > 0 && 10 * c * E < total;
+        flags[e] = over ? 1 : under ? -1 : 0;
+        if (over) atomicAdd(&n_over, 1);
+        if (under) atomicAdd(&n_under, 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        summary[0] = n_over;
+        summary[1] = n_under;
+    }
+}
+
+hipError_t launch_expert_utilization(int E, const int32_t* counts, float* util, int32_t* flags, int32_t* summary,
+                                     hipStream_t stream)
+{
+    expert_utilization_kernel<<<1, 1024, 0, stream>>>(E, counts, util, flags, summary);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -37,11 +37,11 @@ struct GemmArgs {
     const float* As;          // fp8: scales of A rows per 128-K block ([rows, K/128])
     int64_t lda;              // bytes between A rows
     int64_t ldas;             // floats between rows of As
-    const uint8_t* B1;        // routed weights (up: W1, down: W2) [E, N, K]
+    const uint8_t* B1;        // routed weights (up: W1, down: W2) [experts e_base.., N, K]
     const uint8_t* B3;        // up: W3
     const float* B1s;         // fp8 block scales [E, N/128, K/128]
     const float* B3s;
-    const uint8_t* S1;        // shared-expert weights [N_s, K_s]
+    const uint8_t* S1;        // shared-expert weights [N_s rows of ld_s elements, K_s used]
     const uint8_t* S3;
     const float* S1s;
     const float* S3s;
@@ -49,10 +49,13 @@ struct GemmArgs {
     float* outs;              // up with fp8: scales of h [rows, inter_max/128]
     int64_t ldo;              // elements between output rows
     int64_t ldos;             // floats between rows of outs
-    int E;
+    int E;                    // group E is the shared expert
+    int e_base;               // expert held at index 0 of B1/B3 (and their scales)
     int N_r, N_s;             // output features: routed / shared
     int K_r, K_s;             // reduction length: routed / shared
     int n_blocks;             // n-blocks per tile (over the larger N)
+    int64_t ld_s;             // elements between shared weight rows (a slice of a wider expert)
+    int nkb_s;                // fp8: scale blocks between shared scale rows
     int max_tiles;
     int group_m;              // 0: block b -> (tile b / n_blocks, n-block b % n_blocks); else the XCD-aware
                               // grouped order below, with group_m tiles per group
@@ -214,13 +217,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM * 16, wn0 = (wave % WAVES_N) * WN * 16;
-    const int64_t ldb = (int64_t)K * Elem<ET>::bytes;  // bytes per weight row
-    const uint8_t* W1 = shared ? g.S1 : g.B1 + (int64_t)grp * N * ldb;
-    const uint8_t* W3 = UP ? (shared ? g.S3 : g.B3 + (int64_t)grp * N * ldb) : nullptr;
-    const int nkb = K / 128;                           // fp8 weight blocks along K
+    const int64_t ldb = (shared ? g.ld_s : (int64_t)K) * Elem<ET>::bytes;  // bytes per weight row
+    const int64_t lgrp = grp - g.e_base;               // index of the expert in the weight arrays
+    const uint8_t* W1 = shared ? g.S1 : g.B1 + lgrp * N * ldb;
+    const uint8_t* W3 = UP ? (shared ? g.S3 : g.B3 + lgrp * N * ldb) : nullptr;
+    const int nkb = shared ? g.nkb_s : K / 128;        // fp8 scale blocks per weight-scale row
     // fp8: the block scales of this wavefront's output columns (its column span lies in one 128-block)
-    const float* W1s = FP8 ? (shared ? g.S1s : g.B1s + (int64_t)grp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
-    const float* W3s = (FP8 && UP) ? (shared ? g.S3s : g.B3s + (int64_t)grp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
+    const float* W1s = FP8 ? (shared ? g.S1s : g.B1s + lgrp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
+    const float* W3s = (FP8 && UP) ? (shared ? g.S3s : g.B3s + lgrp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
 
     if (tid < BM) s_tok[tid] = tid < rows ? (UP ? g.row_token[row0 + tid] : row0 + tid) : -1;
     __syncthreads();
@@ -447,9 +451,10 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 #endif
 
 // Common fields of both GEMMs' arguments.
-static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws)
+static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws, int e_base)
 {
     GemmArgs a = {};
+    a.e_base = e_base;
     a.tiles = ws.tiles;
     a.ntiles = ws.sync;
     a.max_tiles = (int)ws.max_tiles;
@@ -460,11 +465,11 @@ static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws)
 
 hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, const void* W3, const float* W1s,
                           const float* W3s, const void* S1, const void* S3, const float* S1s, const float* S3s,
-                          const Workspace& ws, hipStream_t stream)
+                          const Workspace& ws, hipStream_t stream, int e_base, int n_shared)
 {
     const bool fp8 = s.w_dtype == MOE_FP8_E4M3, f32 = s.act_dtype == MOE_F32;
     const int64_t act = f32 ? 4 : 2;
-    GemmArgs up = base_args(s, ws);
+    GemmArgs up = base_args(s, ws, e_base);
     up.row_token = ws.row_token;
     up.A = fp8 ? ws.xq : (const uint8_t*)x;
     up.As = ws.xs;
@@ -474,16 +479,19 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     up.B3 = (const uint8_t*)W3;
     up.B1s = W1s;
     up.B3s = W3s;
+    // shared expert: n_shared hidden features, rows of d elements
     up.S1 = (const uint8_t*)S1;
     up.S3 = (const uint8_t*)S3;
     up.S1s = S1s;
     up.S3s = S3s;
+    up.ld_s = s.d;
+    up.nkb_s = (int)(s.d / 128);
     up.out = (uint8_t*)ws.h;
     up.outs = ws.hs;
     up.ldo = ws.inter_max;
     up.ldos = ws.inter_max / 128;
     up.N_r = (int)s.inter;
-    up.N_s = (int)s.inter_shared;
+    up.N_s = n_shared;
     up.K_r = up.K_s = (int)s.d;
     const int bm = tile_rows(s);
     if (fp8) {
@@ -510,30 +518,40 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
 }
 
 hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W2s, const void* S2, const float* S2s,
-                            const Workspace& ws, hipStream_t stream)
+                            const Workspace& ws, hipStream_t stream, int e_base, int n_shared)
 {
     const bool fp8 = s.w_dtype == MOE_FP8_E4M3, f32 = s.act_dtype == MOE_F32;
     const int64_t act = f32 ? 4 : 2;
-    GemmArgs dn = base_args(s, ws);
+    GemmArgs dn = base_args(s, ws, e_base);
     dn.A = (const uint8_t*)ws.h;
     dn.As = ws.hs;
     dn.lda = ws.inter_max * (fp8 ? 1 : act);
     dn.ldas = ws.inter_max / 128;
     dn.B1 = (const uint8_t*)W2;
     dn.B1s = W2s;
+    // shared expert: S2 is [d, n_shared]
     dn.S1 = (const uint8_t*)S2;
     dn.S1s = S2s;
+    dn.ld_s = n_shared;
+    dn.nkb_s = n_shared / 128;
     dn.out = (uint8_t*)ws.y_rows;
     dn.ldo = s.d;
     dn.N_r = dn.N_s = (int)s.d;
     dn.K_r = (int)s.inter;
-    dn.K_s = (int)s.inter_shared;
+    dn.K_s = n_shared;
     const int bm = tile_rows(s);
     if (bm == 16) {
         dn.n_blocks = (int)(s.d / 64);
         if (fp8) launch_one<ET_FP8, false, true, 16, 64, 1, 4>(dn, stream);
         else if (f32) launch_one<ET_F32, false, false, 16, 64, 1, 4>(dn, stream);
         else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
+    } else if (s.d % 256) {
+        // d an odd multiple of 128: 128-wide n-blocks (the wider configurations need d % 256 == 0)
+        dn.n_blocks = (int)(s.d / 128);
+        if (fp8) launch_one<ET_FP8, false, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
+        else if (f32) launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
+        else if (bm == 128) launch_one<ET_BF16, false, true, 128, 128, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(dn, stream);
+        else launch_one<ET_BF16, false, true, 256, 128, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(dn, stream);
     } else if (bm == 128) {
         if (fp8) {
             dn.n_blocks = (int)(s.d / MOE_FP8_DN_BN);

@@ -116,10 +116,11 @@ extern "C" const char* moe_status_string(moe_status_t st)
         if ((expr) != hipSuccess) return MOE_ERR_HIP;    \
     } while (0)
 
-extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
-                                  int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
-                                  int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
-                                  hipStream_t stream)
+// Routing with an optional per-expert mask (allowed == NULL: every expert).
+static moe_status_t route_impl(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                               const uint8_t* allowed, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream)
 {
     moe_status_t st = check_shape(shape);
     if (st != MOE_OK) return st;
@@ -129,14 +130,96 @@ extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const
     if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
     Workspace ws = carve_workspace(s, workspace);
     if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
+    const TileRange all = {0, (int)s.E, 1};
     MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
     if (routing_is_fused(s)) {
-        MOE_TRY(launch_routing_fused(s, ws.logits, idx, w, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws,
-                                     tile_rows(s), stream));
+        MOE_TRY(launch_routing_fused(s, ws.logits, allowed, idx, w, counts, offsets, sorted_slots, pos ? pos : ws.pos,
+                                     ws, tile_rows(s), all, stream));
     } else {
-        MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
-        MOE_TRY(launch_permute(s, idx, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws, tile_rows(s), stream));
+        MOE_TRY(launch_topk(s, ws.logits, allowed, idx, w, ws, stream));
+        MOE_TRY(launch_permute(s, idx, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws, tile_rows(s), all,
+                               stream));
     }
+    return MOE_OK;
+}
+
+extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                                  int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                                  int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream)
+{
+    return route_impl(shape, x, Wg, bias, nullptr, idx, w, counts, offsets, sorted_slots, pos, workspace,
+                      workspace_bytes, stream);
+}
+
+extern "C" moe_status_t moe_route_limited(const moe_shape_t* shape, const void* x, const float* Wg,
+                                          const float* bias, const uint8_t* allowed, int32_t* idx, float* w,
+                                          int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!allowed) return MOE_ERR_INVALID_ARG;
+    return route_impl(shape, x, Wg, bias, allowed, idx, w, counts, offsets, sorted_slots, pos, workspace,
+                      workspace_bytes, stream);
+}
+
+// The layer or one expert-parallel rank's share of it.  Routed experts [e0, e1) (weights of expert e at
+// index e - e0 of W1/W3/W2), n_shared shared hidden features; y (act dtype, rounded) or y_partial (fp32).
+static moe_status_t layer_impl(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                               const uint8_t* allowed, int64_t e0, int64_t e1, int64_t n_shared, const void* W1,
+                               const void* W3, const void* W2, const float* W1s, const float* W3s,
+                               const float* W2s, const void* S1, const void* S3, const void* S2, const float* S1s,
+                               const float* S3s, const float* S2s, void* y, float* y_partial, int32_t* idx_out,
+                               float* w_out, int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, hipEvent_t* events)
+{
+    moe_status_t st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape_t& s = *shape;
+    if (e0 < 0 || e1 > s.E || e0 > e1 || n_shared < 0 || n_shared > s.inter_shared) return MOE_ERR_INVALID_ARG;
+    if (n_shared % 128) return MOE_ERR_UNSUPPORTED;
+    if (s.T == 0) return MOE_OK;
+    const bool routed = e1 > e0, with_shared = n_shared > 0;
+    const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
+    void* out = y ? y : (void*)y_partial;
+    if (!x || !Wg || !out || !workspace) return MOE_ERR_INVALID_ARG;
+    if (routed && (!W1 || !W3 || !W2 || (fp8 && (!W1s || !W3s || !W2s)))) return MOE_ERR_INVALID_ARG;
+    if (with_shared && (!S1 || !S3 || !S2 || (fp8 && (!S1s || !S3s || !S2s)))) return MOE_ERR_INVALID_ARG;
+    if (x == out) return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, out, routed ? W1 : x, routed ? W3 : x, routed ? W2 : x, with_shared ? S1 : x,
+                          with_shared ? S3 : x, with_shared ? S2 : x};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+    Workspace ws = carve_workspace(s, workspace);
+    if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
+
+    int32_t* idx = idx_out ? idx_out : ws.idx;
+    float* w = w_out ? w_out : ws.w;
+    int32_t* counts = counts_out ? counts_out : ws.counts;
+    const TileRange tr = {(int)e0, (int)e1, with_shared ? 1 : 0};
+    const int bm = tile_rows(s);
+    auto mark = [&](int i) -> hipError_t { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
+    MOE_TRY(mark(0));
+    MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
+    MOE_TRY(mark(1));
+    if (routing_is_fused(s)) {
+        MOE_TRY(launch_routing_fused(s, ws.logits, allowed, idx, w, counts, ws.offsets, ws.sorted_slots, ws.pos, ws, bm,
+                                     tr, stream));
+        MOE_TRY(mark(2));
+    } else {
+        MOE_TRY(launch_topk(s, ws.logits, allowed, idx, w, ws, stream));
+        MOE_TRY(mark(2));
+        MOE_TRY(launch_permute(s, idx, counts, ws.offsets, ws.sorted_slots, ws.pos, ws, bm, tr, stream));
+    }
+    MOE_TRY(mark(3));
+    if (fp8) MOE_TRY(launch_act_quant(s, x, ws, stream));
+    MOE_TRY(mark(4));
+    MOE_TRY(launch_up_gemm(s, x, W1, W3, W1s, W3s, S1, S3, S1s, S3s, ws, stream, (int)e0, (int)n_shared));
+    MOE_TRY(mark(5));
+    MOE_TRY(launch_down_gemm(s, W2, W2s, S2, S2s, ws, stream, (int)e0, (int)n_shared));
+    MOE_TRY(mark(6));
+    if (y) MOE_TRY(launch_combine(s, ws.pos, w, ws, y, stream));
+    else MOE_TRY(launch_combine_partial(s, idx, ws.pos, w, ws, (int)e0, (int)e1, with_shared, y_partial, stream));
+    MOE_TRY(mark(7));
     return MOE_OK;
 }
 
@@ -148,46 +231,10 @@ extern "C" moe_status_t moe_forward_staged(const moe_shape_t* shape, const void*
                                            int32_t* counts_out, void* workspace, size_t workspace_bytes,
                                            hipStream_t stream, hipEvent_t* events)
 {
-    moe_status_t st = check_shape(shape);
-    if (st != MOE_OK) return st;
-    const moe_shape_t& s = *shape;
-    if (s.T == 0) return MOE_OK;
-    if (!x || !Wg || !W1 || !W3 || !W2 || !S1 || !S3 || !S2 || !y || !workspace) return MOE_ERR_INVALID_ARG;
-    const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
-    if (fp8 && (!W1s || !W3s || !W2s || !S1s || !S3s || !S2s)) return MOE_ERR_INVALID_ARG;
-    if (x == y) return MOE_ERR_INVALID_ARG;
-    const void* ptrs[] = {x, W1, W3, W2, S1, S3, S2, y};
-    for (const void* p : ptrs)
-        if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
-    Workspace ws = carve_workspace(s, workspace);
-    if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
-
-    int32_t* idx = idx_out ? idx_out : ws.idx;
-    float* w = w_out ? w_out : ws.w;
-    int32_t* counts = counts_out ? counts_out : ws.counts;
-    auto mark = [&](int i) -> hipError_t { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
-    MOE_TRY(mark(0));
-    MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
-    MOE_TRY(mark(1));
-    if (routing_is_fused(s)) {
-        MOE_TRY(launch_routing_fused(s, ws.logits, idx, w, counts, ws.offsets, ws.sorted_slots, ws.pos, ws,
-                                     tile_rows(s), stream));
-        MOE_TRY(mark(2));
-    } else {
-        MOE_TRY(launch_topk(s, ws.logits, idx, w, ws, stream));
-        MOE_TRY(mark(2));
-        MOE_TRY(launch_permute(s, idx, counts, ws.offsets, ws.sorted_slots, ws.pos, ws, tile_rows(s), stream));
-    }
-    MOE_TRY(mark(3));
-    if (fp8) MOE_TRY(launch_act_quant(s, x, ws, stream));
-    MOE_TRY(mark(4));
-    MOE_TRY(launch_up_gemm(s, x, W1, W3, W1s, W3s, S1, S3, S1s, S3s, ws, stream));
-    MOE_TRY(mark(5));
-    MOE_TRY(launch_down_gemm(s, W2, W2s, S2, S2s, ws, stream));
-    MOE_TRY(mark(6));
-    MOE_TRY(launch_combine(s, ws.pos, w, ws, y, stream));
-    MOE_TRY(mark(7));
-    return MOE_OK;
+    if (!shape) return MOE_ERR_INVALID_ARG;
+    return layer_impl(shape, x, Wg, bias, nullptr, 0, shape->E, shape->inter_shared, W1, W3, W2, W1s, W3s, W2s, S1,
+                      S3, S2, S1s, S3s, S2s, y, nullptr, idx_out, w_out, counts_out, workspace, workspace_bytes,
+                      stream, events);
 }
 
 extern "C" moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
@@ -199,4 +246,26 @@ extern "C" moe_status_t moe_forward(const moe_shape_t* shape, const void* x, con
 {
     return moe_forward_staged(shape, x, Wg, bias, W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s, S2s, y, idx_out,
                               w_out, counts_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" moe_status_t moe_forward_shard(const moe_shape_t* shape, const void* x, const float* Wg,
+                                          const float* bias, const uint8_t* allowed, int64_t e0, int64_t e1,
+                                          int64_t n_shared, const void* W1, const void* W3, const void* W2,
+                                          const float* W1s, const float* W3s, const float* W2s, const void* S1,
+                                          const void* S3, const void* S2, const float* S1s, const float* S3s,
+                                          const float* S2s, float* y_partial, int32_t* idx_out, float* w_out,
+                                          int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream)
+{
+    return layer_impl(shape, x, Wg, bias, allowed, e0, e1, n_shared, W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s,
+                      S2s, nullptr, y_partial, idx_out, w_out, counts_out, workspace, workspace_bytes, stream,
+                      nullptr);
+}
+
+extern "C" moe_status_t moe_expert_utilization(int64_t E, const int32_t* counts, float* util, int32_t* flags,
+                                               int32_t* summary, hipStream_t stream)
+{
+    if (E <= 0 || E > (1 << 30) || !counts || !util || !flags || !summary) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_expert_utilization((int)E, counts, util, flags, summary, stream));
+    return MOE_OK;
 }

@@ -100,6 +100,11 @@ struct Workspace {
     int64_t max_tiles, nchunks, inter_max;
 };
 
+// Groups that get GEMM tiles: routed experts [g0, g1), and the shared expert when `shared` is set.
+struct TileRange {
+    int g0, g1, shared;
+};
+
 // Rows per grouped-GEMM tile for this shape.
 int tile_rows(const moe_shape_t& s);
 
@@ -111,20 +116,28 @@ Workspace carve_workspace(const moe_shape_t& s, void* base);
 // ------------------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
                                 float* logits, hipStream_t stream);
-hipError_t launch_topk(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, const Workspace& ws,
-                       hipStream_t stream);
+hipError_t launch_topk(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
+                       const Workspace& ws, hipStream_t stream);
 bool routing_is_fused(const moe_shape_t& s);
-hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, int32_t* counts,
-                                int32_t* offsets, int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm,
-                                hipStream_t stream);
+hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
+                                int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos,
+                                const Workspace& ws, int bm, TileRange tr, hipStream_t stream);
 hipError_t launch_permute(const moe_shape_t& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm, hipStream_t stream);
+                          int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm, TileRange tr,
+                          hipStream_t stream);
 hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace& ws, hipStream_t stream);
+// e_base: the expert stored first in W1/W3/W2 (0 for the whole layer); n_shared: the shared hidden
+// features held in S1/S3 ([n_shared, d]) and S2 ([d, n_shared]).
 hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, const void* W3, const float* W1s,
                           const float* W3s, const void* S1, const void* S3, const float* S1s, const float* S3s,
-                          const Workspace& ws, hipStream_t stream);
+                          const Workspace& ws, hipStream_t stream, int e_base, int n_shared);
 hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W2s, const void* S2, const float* S2s,
-                            const Workspace& ws, hipStream_t stream);
+                            const Workspace& ws, hipStream_t stream, int e_base, int n_shared);
+hipError_t launch_combine_partial(const moe_shape_t& s, const int32_t* idx, const int32_t* pos, const float* w,
+                                  const Workspace& ws, int e0, int e1, int with_shared, float* y_partial,
+                                  hipStream_t stream);
+hipError_t launch_expert_utilization(int E, const int32_t* counts, float* util, int32_t* flags, int32_t* summary,
+                                     hipStream_t stream);
 hipError_t launch_combine(const moe_shape_t& s, const int32_t* pos, const float* w, const Workspace& ws, void* y,
                           hipStream_t stream);
 

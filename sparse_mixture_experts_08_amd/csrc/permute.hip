@@ -21,18 +21,18 @@ namespace moe {
 constexpr int kFusedMaxTokens = 256;
 
 // Tile list for groups with counts cnt[0..E) and offsets off[0..E]: shared expert (group E, rows
-// [T*k, T*k + T)) first, then experts ascending, each cut into bm-row tiles.  One thread per expert;
-// called by all NT threads of the block.
+// [T*k, T*k + T)) first when `shared` is set, then the experts of [g0, g1) ascending, each cut into
+// bm-row tiles.  One thread per expert; called by all NT threads of the block.
 template <int NT>
-__device__ void write_tiles(const int* cnt, const int* off, int E, int T, int k, int bm, int4* tiles, int32_t* ntiles,
-                            int* scan_lds)
+__device__ void write_tiles(const int* cnt, const int* off, int E, int T, int k, int bm, TileRange tr, int4* tiles,
+                            int32_t* ntiles, int* scan_lds)
 {
-    const int nshared = (T + bm - 1) / bm;
+    const int nshared = tr.shared ? (T + bm - 1) / bm : 0;
     for (int i = threadIdx.x; i < nshared; i += NT) tiles[i] = make_int4(E, T * k + i * bm, min(bm, T - i * bm), 0);
     int carry = nshared;
     for (int e0 = 0; e0 < E; e0 += NT) {
         const int e = e0 + threadIdx.x;
-        const int c = e < E ? cnt[e] : 0;
+        const int c = (e < E && e >= tr.g0 && e < tr.g1) ? cnt[e] : 0;
         const int nt = (c + bm - 1) / bm;
         int total;
         const int base = carry + block_exclusive_scan<NT>(nt, &total, scan_lds);
@@ -45,7 +45,8 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int k,
 // ---------------------------------------------------------------------------------------------------
 // Fused path (T <= 256): one block of 1024 threads.
 // ---------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restrict__ L, int T, int E, int k, int bm,
+__global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restrict__ L, const uint8_t* __restrict__ allowed,
+                                                           int T, int E, int k, int bm, TileRange tr,
                                                            int32_t* __restrict__ idx, float* __restrict__ w,
                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_slots, int32_t* __restrict__ pos,
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restri
             const bool valid = t < T;
             int my_e;
             float my_w;
-            topk_group<16, 16>(L + (size_t)(valid ? t : 0) * E, E, k, sub, my_e, my_w);
+            topk_group<16, 16>(L + (size_t)(valid ? t : 0) * E, allowed, E, k, sub, my_e, my_w);
             if (valid && sub < k) {
                 idx[(size_t)t * k + sub] = my_e;
                 w[(size_t)t * k + sub] = my_w;
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restri
         for (int t = wave; t < T; t += 16) {
             int my_e;
             float my_w;
-            topk_group<64, 16>(L + (size_t)t * E, E, k, lane, my_e, my_w);
+            topk_group<64, 16>(L + (size_t)t * E, allowed, E, k, lane, my_e, my_w);
             if (lane < k) {
                 idx[(size_t)t * k + lane] = my_e;
                 w[(size_t)t * k + lane] = my_w;
@@ -129,14 +130,14 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restri
         row_token[p] = t;
     }
     for (int t = tid; t < T; t += 1024) row_token[T * k + t] = t;
-    write_tiles<1024>(cnt, off, E, T, k, bm, tiles, sync, scan_lds);
+    write_tiles<1024>(cnt, off, E, T, k, bm, tr, tiles, sync, scan_lds);
 }
 
 // ---------------------------------------------------------------------------------------------------
 // Multi-block path.
 // ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int E,
-                                                         int T, int k, int bm, int32_t* __restrict__ chunk_prefix,
+                                                         int T, int k, int bm, TileRange tr, int32_t* __restrict__ chunk_prefix,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int4* __restrict__ tiles, int32_t* __restrict__ sync)
 {
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t* __restri
         sync[1] = 0;
     }
     __syncthreads();
-    write_tiles<256>(cnt, off, E, T, k, bm, tiles, sync, scan_lds);
+    write_tiles<256>(cnt, off, E, T, k, bm, tr, tiles, sync, scan_lds);
 }
 
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, const uint64_t* __restrict__ chunk_bits,
@@ -209,20 +210,21 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 
 bool routing_is_fused(const moe_shape_t& s) { return s.T <= kFusedMaxTokens; }
 
-hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, int32_t* counts,
-                                int32_t* offsets, int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm,
-                                hipStream_t stream)
+hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
+                                int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos,
+                                const Workspace& ws, int bm, TileRange tr, hipStream_t stream)
 {
-    route_fused_kernel<<<1, 1024, 0, stream>>>(logits, (int)s.T, (int)s.E, (int)s.k, bm, idx, w, counts, offsets,
+    route_fused_kernel<<<1, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, bm, tr, idx, w, counts, offsets,
                                                sorted_slots, pos, ws.row_token, ws.tiles, ws.sync);
     return hipGetLastError();
 }
 
 hipError_t launch_permute(const moe_shape_t& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm, hipStream_t stream)
+                          int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm, TileRange tr,
+                          hipStream_t stream)
 {
     const int T = (int)s.T, E = (int)s.E, k = (int)s.k, nch = (int)ws.nchunks;
-    chunk_scan_kernel<<<E, 256, 0, stream>>>(ws.chunk_counts, nch, E, T, k, bm, ws.chunk_prefix, counts, offsets,
+    chunk_scan_kernel<<<E, 256, 0, stream>>>(ws.chunk_counts, nch, E, T, k, bm, tr, ws.chunk_prefix, counts, offsets,
                                              ws.tiles, ws.sync);
     scatter_kernel<<<nch, 64, 0, stream>>>(idx, ws.chunk_bits, ws.chunk_prefix, offsets, T, E, k, sorted_slots, pos,
                                            ws.row_token);

@@ -248,7 +248,8 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
 // Top-k + softmax for many tokens: one wavefront per token, 64 tokens (one chunk) per block of 16
 // wavefronts.  Also records, per chunk, which tokens chose each expert (a 64-bit mask) and how many.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restrict__ L, int T, int E, int k,
+__global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restrict__ L, const uint8_t* __restrict__ allowed,
+                                                            int T, int E, int k,
                                                             int32_t* __restrict__ idx, float* __restrict__ w,
                                                             uint64_t* __restrict__ chunk_bits,
                                                             int32_t* __restrict__ chunk_counts,
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
         if (t >= T) break;
         int my_e;
         float my_w;
-        topk_group<64, 16>(L + (size_t)t * E, E, k, lane, my_e, my_w);
+        topk_group<64, 16>(L + (size_t)t * E, allowed, E, k, lane, my_e, my_w);
         if (lane < k) {
             idx[(size_t)t * k + lane] = my_e;
             w[(size_t)t * k + lane] = my_w;
@@ -280,10 +281,10 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
     }
 }
 
-hipError_t launch_topk(const moe_shape_t& s, const float* logits, int32_t* idx, float* w, const Workspace& ws,
-                       hipStream_t stream)
+hipError_t launch_topk(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
+                       const Workspace& ws, hipStream_t stream)
 {
-    topk_softmax_kernel<<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, (int)s.T, (int)s.E, (int)s.k, idx, w,
+    topk_softmax_kernel<<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, idx, w,
                                                                      ws.chunk_bits, ws.chunk_counts, ws.sync);
     return hipGetLastError();
 }

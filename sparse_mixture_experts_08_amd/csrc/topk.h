@@ -13,6 +13,8 @@
 
 namespace moe {
 
+// Order-preserving map of a float (finite or -inf) to uint32; +0 and -0 map to the same key, and every
+// key is nonzero.
 __device__ __forceinline__ uint32_t ordered_bits(float f)
 {
     uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
@@ -39,17 +41,25 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t v)
     return v;
 }
 
+// The logit of expert e after the optional device-limited routing mask: -inf where allowed[e] == 0
+// (the page's `logits + mask` with mask -inf outside the allowed experts, 0 inside).
+__device__ __forceinline__ float masked_logit(const float* __restrict__ Lrow, const uint8_t* __restrict__ allowed, int e)
+{
+    return (allowed && !allowed[e]) ? -INFINITY : Lrow[e];
+}
+
 // Top-k of row L[0..E) held by a group of W lanes (sub = lane index in the group), each lane holding the
 // logits e = sub + W * q for q < NQ (NQ * W >= E).  On return, lane sub < k of the group holds slot
-// sub's expert and weight.  k <= min(W, 16).
+// sub's expert and weight.  k <= min(W, 16).  allowed (nullable): the routing mask.
 template <int W, int NQ>
-__device__ __forceinline__ void topk_group(const float* __restrict__ Lrow, int E, int k, int sub, int& my_e, float& my_w)
+__device__ __forceinline__ void topk_group(const float* __restrict__ Lrow, const uint8_t* __restrict__ allowed, int E,
+                                           int k, int sub, int& my_e, float& my_w)
 {
     uint64_t key[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; q++) {
         const int e = sub + W * q;
-        key[q] = e < E ? logit_key(Lrow[e], e) : 0ull;
+        key[q] = e < E ? logit_key(masked_logit(Lrow, allowed, e), e) : 0ull;
     }
     my_e = 0;
     float my_l = 0.0f;
@@ -66,7 +76,7 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ Lrow, int E
         }
         if (sub == j) {
             my_e = e;
-            my_l = Lrow[e];
+            my_l = masked_logit(Lrow, allowed, e);
         }
     }
     const float m = __shfl(my_l, 0, W);

@@ -101,3 +101,49 @@ def test_status_strings():
     for st in range(5):
         assert B.moe_status_string(st)
     assert "workspace" in B.moe_status_string(3)
+
+
+def _call_shard(shape, e0, e1, n_shared, ptrs=None, ws_bytes=1 << 30):
+    # x, Wg, bias, allowed | W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s, S2s, y_partial, idx, w, counts, ws
+    L = B.lib()
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(21)] if ptrs is None else ptrs
+    return L.moe_forward_shard(ctypes.byref(shape), *p[:4], e0, e1, n_shared, *p[4:], ctypes.c_size_t(ws_bytes), None)
+
+
+def test_shard_argument_errors_are_host_side():
+    s = _shape()
+    assert _call_shard(s, 0, 257, 2048) == 1            # e1 > E
+    assert _call_shard(s, 9, 8, 2048) == 1              # e0 > e1
+    assert _call_shard(s, -1, 8, 2048) == 1
+    assert _call_shard(s, 0, 8, 4096) == 1              # more shared features than the expert has
+    assert _call_shard(s, 0, 8, 100) == 2               # not a multiple of 128
+    assert _call_shard(_shape(d=7100), 0, 8, 128) == 2
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(21)]
+    p[16] = None                                         # y_partial
+    assert _call_shard(s, 0, 8, 128, p) == 1
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(21)]
+    p[4] = None                                          # W1 with a non-empty expert range
+    assert _call_shard(s, 0, 8, 128, p) == 1
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(21)]
+    p[10] = None                                         # S1 with a shared slice
+    assert _call_shard(s, 0, 8, 128, p) == 1
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(21)]
+    p[16] = p[0]                                         # y_partial aliasing x
+    assert _call_shard(s, 0, 8, 128, p) == 1
+    assert _call_shard(s, 0, 8, 128, ws_bytes=4096) == 3
+    # T = 0 with empty ranges and no pointers: a no-op
+    assert _call_shard(_shape(T=0), 0, 0, 0, [None] * 21, ws_bytes=0) == 0
+
+
+def test_route_limited_and_utilization_argument_errors():
+    L = B.lib()
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(11)]
+    p[3] = None                                          # allowed is required
+    assert L.moe_route_limited(ctypes.byref(_shape()), *p, ctypes.c_size_t(1 << 30), None) == 1
+    assert L.moe_route_limited(ctypes.byref(_shape(k=9, E=8)), *([ctypes.c_void_p(16)] * 11),
+                               ctypes.c_size_t(1 << 30), None) == 1
+    q = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(4)]
+    assert L.moe_expert_utilization(0, *q, None) == 1
+    assert L.moe_expert_utilization(-3, *q, None) == 1
+    q[2] = None
+    assert L.moe_expert_utilization(8, *q, None) == 1

@@ -18,11 +18,13 @@ SMALL = [
     W.Workload("small-bf16-decode", 200, 1024, 64, 6, 384, 256, BF16, BF16),   # 16-row tiles, ragged
     W.Workload("small-bf16-prefill", 600, 512, 16, 4, 256, 384, BF16, BF16),   # 128-row tiles, ragged
     W.Workload("small-f32-prefill", 600, 512, 16, 4, 256, 256, F32, F32),
-    W.Workload("small-bf16-bigtile", 1100, 512, 8, 2, 256, 384, BF16, BF16),   # 256-row tiles
+    W.Workload("small-bf16-bigtile", 1100, 512, 8, 2, 256, 384, BF16, BF16),   # ~275 rows per expert
     W.Workload("small-fp8-decode", 150, 1024, 32, 4, 512, 256, BF16, FP8),
     W.Workload("small-fp8-prefill", 700, 512, 16, 4, 256, 384, BF16, FP8),
     W.Workload("small-skew-bf16", 300, 512, 64, 8, 256, 256, BF16, BF16, skew=True),
     W.Workload("tiny-E256-T5", 5, 512, 256, 8, 256, 256, BF16, BF16),     # few tokens over many experts
+    W.Workload("small-bf16-d384", 600, 384, 16, 4, 256, 384, BF16, BF16),     # d an odd multiple of 128
+    W.Workload("small-fp8-d384", 500, 384, 16, 4, 256, 256, BF16, FP8),
 ]
 
 
