@@ -1,11 +1,17 @@
 """Benchmark of the MoE feed-forward layer forward pass on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--variant V] [--no-cpu-baseline]
 
 A step is one moe_forward call (router, top-k, permutation, grouped up GEMM with the shared expert,
 grouped down GEMM, combine) over one batch of synthetic tokens already resident in HBM.  Prints one JSON
 line: tokens/s, the dominant kernel's roofline figures (its average duration from HIP events recorded
 around it on the launch stream, over the timed steps) and the CPU oracle timed on a bounded sample.
+
+--variant selects another entry point on the same workload (one JSON line each):
+  shard-ep8      moe_forward_shard of one of 8 expert-parallel ranks (E/8 experts, 1/8 of the shared
+                 expert's features; the all-reduce over ranks is not part of it)
+  route-limited  moe_route_limited with the experts of one of 8 devices allowed
+  utilization    moe_expert_utilization over the workload's expert counts
 """
 import argparse
 import ctypes
@@ -26,6 +32,7 @@ from sparse_mixture_experts_08_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {W.BF16: 2500.0, W.FP8_E4M3: 5000.0, W.F32: 157.3}
+FP32_VALU_PEAK_TFLOPS = 157.3  # 256 CUs x 2.4 GHz x 256 fp32 flops/clock (packed FMA counted)
 
 
 class HipEvents:
@@ -56,20 +63,31 @@ class HipEvents:
             self.hip.hipEventDestroy(self.arr[i])
 
 
-def algorithmic(wl, counts):
-    """Algorithmic bytes and flops of the up GEMM, the down GEMM and the whole layer for this routing."""
+def algorithmic(wl, counts, e0=0, e1=None, n_shared=None):
+    """Algorithmic bytes and flops of the up GEMM, the down GEMM and the whole call for this routing, over
+    the routed experts [e0, e1) and n_shared shared features (default: the whole layer)."""
+    e1 = wl.E if e1 is None else e1
+    n_shared = wl.inter_shared if n_shared is None else n_shared
     wb = {W.F32: 4, W.BF16: 2, W.FP8_E4M3: 1}[wl.w_dtype]
     ab = 4 if wl.act_dtype == W.F32 else 2
-    touched = int((counts > 0).sum())
-    rows = wl.T * wl.k + wl.T
+    c = counts[e0:e1]
+    touched = int((c > 0).sum())
+    routed_rows = int(c.sum())
+    shared_rows = wl.T if n_shared else 0
+    rows = routed_rows + shared_rows
     sblk = 4.0 / (128 * 128) if wl.w_dtype == W.FP8_E4M3 else 0.0      # fp32 block scale per 128x128
-    up_w = (touched * wl.inter + wl.inter_shared) * 2 * wl.d * (wb + sblk)
-    dn_w = (touched * wl.inter + wl.inter_shared) * wl.d * (wb + sblk)
-    up_bytes = up_w + wl.T * wl.d * ab + rows * (wl.inter if wl.inter >= wl.inter_shared else wl.inter_shared) * ab
-    dn_bytes = dn_w + rows * wl.d * ab
-    up_flops = 2.0 * 2 * wl.d * (wl.T * wl.k * wl.inter + wl.T * wl.inter_shared)
-    dn_flops = 2.0 * wl.d * (wl.T * wl.k * wl.inter + wl.T * wl.inter_shared)
-    layer_bytes = up_w + dn_w + wl.d * wl.E * 4 + 2 * wl.T * wl.d * ab
+    up_w = (touched * wl.inter + n_shared) * 2 * wl.d * (wb + sblk)
+    dn_w = (touched * wl.inter + n_shared) * wl.d * (wb + sblk)
+    # h is written by the up GEMM and read by the down GEMM; fp8 weights store it as E4M3 codes
+    hb = 1 + 4.0 / 128 if wl.w_dtype == W.FP8_E4M3 else ab
+    h_bytes = (routed_rows * wl.inter + shared_rows * n_shared) * hb
+    up_bytes = up_w + wl.T * wl.d * ab + h_bytes
+    dn_bytes = dn_w + h_bytes + rows * wl.d * ab
+    up_flops = 2.0 * 2 * wl.d * (routed_rows * wl.inter + shared_rows * n_shared)
+    dn_flops = 2.0 * wl.d * (routed_rows * wl.inter + shared_rows * n_shared)
+    full = e0 == 0 and e1 == wl.E and n_shared == wl.inter_shared
+    out_b = wl.T * wl.d * (ab if full else 4)
+    layer_bytes = up_w + dn_w + wl.d * wl.E * 4 + wl.T * wl.d * ab + out_b
     return dict(touched=touched, up_bytes=up_bytes, dn_bytes=dn_bytes, up_flops=up_flops, dn_flops=dn_flops,
                 layer_bytes=layer_bytes, layer_flops=up_flops + dn_flops + 2.0 * wl.T * wl.d * wl.E)
 
@@ -89,9 +107,10 @@ def measured_traffic(workload, kernel):
     return None if not k else k["bytes"]
 
 
-def cpu_baseline(wl, inp, max_tokens):
+def cpu_baseline(wl, inp, max_tokens, shard=None):
     """The CPU oracle on a bounded sample of the same workload: routing of every token plus experts and
-    combine for up to max_tokens tokens; tokens/s from the per-token cost of both parts."""
+    combine for up to max_tokens tokens; tokens/s from the per-token cost of both parts.  With shard =
+    (e0, e1, s0, s1): the oracle's expert-parallel partial of that rank instead of the whole layer."""
     from oracle import oracle as O
     h = {n: W.to_numpy(t) for n, t in inp.items()}
     t0 = time.perf_counter()
@@ -101,13 +120,226 @@ def cpu_baseline(wl, inp, max_tokens):
     toks = np.arange(n, dtype=np.int32)
     sc = {k: h.get(k) for k in ("W1s", "W3s", "W2s", "S1s", "S3s", "S2s")}
     t0 = time.perf_counter()
-    O.forward(wl.shape(), h["x"], h["W1"], h["W3"], h["W2"], h["S1"], h["S3"], h["S2"], r["idx"], r["w"],
-              tokens=toks, **sc)
+    if shard is None:
+        O.forward(wl.shape(), h["x"], h["W1"], h["W3"], h["W2"], h["S1"], h["S3"], h["S2"], r["idx"], r["w"],
+                  tokens=toks, **sc)
+    else:
+        O.forward_shard(wl.shape(), h["x"], h["W1"], h["W3"], h["W2"], h["S1"], h["S3"], h["S2"], r["idx"],
+                        r["w"], *shard, tokens=toks, **sc)
     t_fwd = time.perf_counter() - t0
     per_token = t_route / wl.T + t_fwd / n
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"routing of all {wl.T} tokens ({t_route:.2f} s) + experts and combine of {n} tokens "
                       f"({t_fwd:.2f} s); tokens/s = 1 / (route s/token + expert s/token)"}
+
+
+def roofline_of(bytes_, flops, ms, peak_tflops, kernel):
+    """Roofline figures of one kernel: bound by whichever of HBM bytes and MFMA flops takes longer at peak."""
+    if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (peak_tflops * 1e12):
+        roof = {"bound": "hbm", "achieved": bytes_ / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12, "peak": peak_tflops, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = kernel
+    roof["kernel_ms"] = ms
+    return roof
+
+
+def wall_ms(fn, steps, warmup):
+    """Wall-clock ms per call of fn over `steps` calls after `warmup`, synchronised on both sides."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def staged_ms(fn, steps):
+    """Mean device ms of each stage: fn(events) records NUM_STAGES + 1 HIP events on the launch stream."""
+    ns = B.NUM_STAGES
+    ev = HipEvents((ns + 1) * steps)
+    for s in range(steps):
+        fn((ctypes.c_void_p * (ns + 1)).from_buffer(ev.arr, s * (ns + 1) * ctypes.sizeof(ctypes.c_void_p)))
+    torch.cuda.synchronize()
+    stage = np.zeros(ns)
+    for s in range(steps):
+        for i in range(ns):
+            stage[i] += ev.elapsed_ms(s * (ns + 1) + i, s * (ns + 1) + i + 1)
+    ev.close()
+    return stage / steps
+
+
+def event_ms(fn, steps):
+    """Mean device ms of one fn() call from HIP events recorded around each call on torch's stream."""
+    ev = HipEvents(2 * steps)
+    hip = ev.hip
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for s in range(steps):
+        hip.hipEventRecord(ev.arr[2 * s], stream)
+        fn()
+        hip.hipEventRecord(ev.arr[2 * s + 1], stream)
+    torch.cuda.synchronize()
+    ms = sum(ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(steps)) / steps
+    ev.close()
+    return ms
+
+
+def ep8_ranges(wl, rank):
+    """Experts and shared features of expert-parallel rank `rank` of 8."""
+    if wl.E % 8 or wl.inter_shared % (8 * 128):
+        raise SystemExit(f"{wl.name}: E and inter_shared / 128 must split 8 ways for shard-ep8")
+    ne, ns = wl.E // 8, wl.inter_shared // 8
+    return rank * ne, (rank + 1) * ne, rank * ns, (rank + 1) * ns
+
+
+def base_record(wl, args, metric, value, unit, ms, higher=True):
+    return {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": higher, "scaling": "weak", "vs_baseline": None,
+        "dtype": {W.F32: "f32", W.BF16: "bf16", W.FP8_E4M3: "fp8_e4m3"}[wl.w_dtype], "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "inter": wl.inter,
+                   "inter_shared": wl.inter_shared, "parallelism": "none (one GPU)"},
+    }
+
+
+def run_layer(wl, inp, args, dev):
+    shape = B.make_shape(wl.T, wl.d, wl.E, wl.k, wl.inter, wl.inter_shared, wl.act_dtype, wl.w_dtype)
+    ws = torch.empty(B.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    shard = None
+    if args.variant == "shard-ep8":
+        shard = ep8_ranges(wl, args.rank)
+        lw = B.shard_weights(inp, *shard)
+        e0, e1, s0, s1 = shard
+        yp = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
+        sc = {n: lw[n] for n in ("W1s", "W3s", "W2s", "S1s", "S3s", "S2s") if n in lw} or None
+
+        def call(events=None, routing=False):
+            return B.moe_forward_shard(inp["x"], inp["Wg"], inp.get("bias"), wl.k, e0, e1, lw["W1"], lw["W3"],
+                                       lw["W2"], lw["S1"], lw["S3"], lw["S2"], wl.inter, wl.inter_shared,
+                                       scales=sc, y_partial=yp, workspace=ws, routing=routing, events=events)
+    else:
+        y = torch.empty_like(inp["x"])
+
+        def call(events=None, routing=False):
+            return B.forward_inputs(inp, wl.k, y=y, workspace=ws, routing=routing, events=events)
+    _, r = call(routing=True)
+    torch.cuda.synchronize()
+    counts = r["counts"].cpu().numpy()
+    alg = algorithmic(wl, counts) if shard is None else algorithmic(wl, counts, shard[0], shard[1],
+                                                                    shard[3] - shard[2])
+    ms_per_step = wall_ms(call, args.steps, args.warmup)
+    stage_ms = staged_ms(lambda ev: call(events=ev), args.steps)
+    up_ms, dn_ms = stage_ms[4], stage_ms[5]
+    roof = roofline_of(alg["up_bytes"], alg["up_flops"], up_ms, MFMA_PEAK_TFLOPS[wl.w_dtype],
+                       "grouped up GEMM (W1, W3, SiLU*mul; routed + shared)")
+    roof["traffic"] = measured_traffic(wl.name if shard is None else f"{wl.name}/shard-ep8", "up_gemm")
+    # keep the documented key order: bound, achieved, peak, unit, frac, traffic
+    roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel", "kernel_ms")}
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if shard is None:
+        metric = "MoE-layer tokens/s at d=7168, 256 experts top-8; % of HBM or MFMA roofline"
+    else:
+        metric = (f"expert-parallel rank {args.rank}/8 tokens/s (experts [{shard[0]},{shard[1]}), shared features "
+                  f"[{shard[2]},{shard[3]}); fp32 partial, all-reduce excluded)")
+    out = base_record(wl, args, metric, wl.T / (ms_per_step * 1e-3), "tokens/s", ms_per_step)
+    if shard is not None:
+        out["config"]["parallelism"] = f"ep8 rank {args.rank} (one GPU's share)"
+    out["roofline"] = roof
+    out["layer"] = {"algorithmic_GB": alg["layer_bytes"] / 1e9, "touched_experts": alg["touched"],
+                    "GB_per_s": alg["layer_bytes"] / (ms_per_step * 1e-3) / 1e9,
+                    "hbm_frac": alg["layer_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "TFLOP_per_s": alg["layer_flops"] / (ms_per_step * 1e-3) / 1e12,
+                    "stage_ms": {n: float(v) for n, v in zip(B.STAGE_NAMES, stage_ms)},
+                    "down_gemm_GB_per_s": alg["dn_bytes"] / (dn_ms * 1e-3) / 1e9 if dn_ms > 0 else None}
+    out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens, shard)
+    return out
+
+
+def run_route_limited(wl, inp, args, dev):
+    # the experts of device `rank` of 8 (contiguous blocks of E/8), as a device_expert_map would list them
+    ne = max(wl.E // 8, wl.k)
+    allowed = torch.zeros(wl.E, dtype=torch.uint8)
+    allowed[args.rank * ne:(args.rank + 1) * ne] = 1
+    a_dev = allowed.to(dev)
+    shape = B.make_shape(wl.T, wl.d, wl.E, wl.k, 128, 128, wl.act_dtype, wl.act_dtype)
+    ws = torch.empty(B.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    call = lambda: B.moe_route_limited(inp["x"], inp["Wg"], inp.get("bias"), a_dev, wl.k, workspace=ws)  # noqa
+    ms_per_step = wall_ms(call, args.steps, args.warmup)
+    dev_ms = event_ms(call, args.steps)
+    ab = 4 if wl.act_dtype == W.F32 else 2
+    bytes_ = wl.T * wl.d * ab + wl.d * wl.E * 4 + wl.E + wl.T * wl.k * (4 + 4 + 4 + 4) + (2 * wl.E + 1) * 4
+    flops = 2.0 * wl.T * wl.d * wl.E
+    # the router's fp32 FMA chains run on the vector ALUs (bit-exact logits), not on MFMA
+    if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (FP32_VALU_PEAK_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": bytes_ / (dev_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "alu", "achieved": flops / (dev_ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "whole moe_route_limited call (router logits + masked top-k + permutation)"
+    roof["kernel_ms"] = dev_ms
+    out = base_record(wl, args, f"device-limited routing tokens/s ({int(allowed.sum())} of {wl.E} experts allowed)",
+                      wl.T / (ms_per_step * 1e-3), "tokens/s", ms_per_step)
+    out["roofline"] = roof
+    out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        h = {n: W.to_numpy(inp[n]) for n in ("x", "Wg")}
+        t0 = time.perf_counter()
+        O.route_limited(h["x"], h["Wg"], W.to_numpy(inp.get("bias")), allowed.numpy(), wl.k, wl.act_dtype)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": wl.T / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+                               "sample": f"route_limited of all {wl.T} tokens ({dt:.2f} s)"}
+    return out
+
+
+def run_utilization(wl, inp, args, dev):
+    r = B.moe_route(inp["x"], inp["Wg"], inp.get("bias"), wl.k)
+    counts = r["counts"]
+    util = torch.empty(wl.E, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    call = lambda: B.moe_expert_utilization(counts)  # noqa: E731
+    steps = max(args.steps, 200)
+    ms_per_step = wall_ms(call, steps, args.warmup)
+    dev_ms = event_ms(call, steps)
+    bytes_ = wl.E * (4 + 4 + 4) + 8
+    roof = {"bound": "hbm", "achieved": bytes_ / (dev_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "expert_utilization_kernel (one block; launch-latency bound at this size)"
+    roof["kernel_ms"] = dev_ms
+    out = base_record(wl, args, "expert-utilisation monitor latency per call (us)", ms_per_step * 1e3, "us",
+                      ms_per_step, higher=False)
+    out["steps"] = steps
+    out["roofline"] = roof
+    out["cpu_baseline"] = None
+    del util
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        c = counts.cpu().numpy()
+        n = 2000
+        t0 = time.perf_counter()
+        for _ in range(n):
+            O.expert_utilization(c)
+        dt = (time.perf_counter() - t0) / n
+        out["cpu_baseline"] = {"value": dt * 1e6, "unit": "us", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} calls of expert_utilization on the same {wl.E} counts"}
+    return out
 
 
 def main():
@@ -116,6 +348,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=W.DECODE_BF16.name, choices=[w.name for w in W.CONFIGS])
+    ap.add_argument("--variant", default="layer", choices=["layer", "shard-ep8", "route-limited", "utilization"])
+    ap.add_argument("--rank", type=int, default=0, choices=range(8), help="expert-parallel rank / device (of 8)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -134,87 +368,13 @@ def main():
     wl = W.BY_NAME[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    inp = W.generate(wl, seed=args.seed, device=dev)
-    shape = B.make_shape(wl.T, wl.d, wl.E, wl.k, wl.inter, wl.inter_shared, wl.act_dtype, wl.w_dtype)
-    ws = torch.empty(B.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
-    y = torch.empty_like(inp["x"])
-    _, r = B.forward_inputs(inp, wl.k, y=y, workspace=ws, routing=True)
-    torch.cuda.synchronize()
-    alg = algorithmic(wl, r["counts"].cpu().numpy())
-
-    # headline: plain moe_forward steps
-    for _ in range(args.warmup):
-        B.forward_inputs(inp, wl.k, y=y, workspace=ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        B.forward_inputs(inp, wl.k, y=y, workspace=ws)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = dt * 1e3 / args.steps
-
-    # per-stage device time: HIP events recorded between stages on the launch stream
-    ns = B.NUM_STAGES
-    ev = HipEvents((ns + 1) * args.steps)
-    for s in range(args.steps):
-        sub = (ctypes.c_void_p * (ns + 1)).from_buffer(ev.arr, s * (ns + 1) * ctypes.sizeof(ctypes.c_void_p))
-        B.forward_inputs(inp, wl.k, y=y, workspace=ws, events=sub)
-    torch.cuda.synchronize()
-    stage_ms = np.zeros(ns)
-    for s in range(args.steps):
-        for i in range(ns):
-            stage_ms[i] += ev.elapsed_ms(s * (ns + 1) + i, s * (ns + 1) + i + 1)
-    stage_ms /= args.steps
-    ev.close()
-
-    up_ms, dn_ms = stage_ms[4], stage_ms[5]
-    # the binding roofline of the up GEMM: the larger of its HBM time and its MFMA time at peak
-    hbm_bound = alg["up_bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["up_flops"] / (MFMA_PEAK_TFLOPS[wl.w_dtype] * 1e12)
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": alg["up_bytes"] / (up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
+    inp = W.generate(wl, seed=args.seed, device=dev, weights=args.variant in ("layer", "shard-ep8"))
+    if args.variant in ("layer", "shard-ep8"):
+        out = run_layer(wl, inp, args, dev)
+    elif args.variant == "route-limited":
+        out = run_route_limited(wl, inp, args, dev)
     else:
-        roof = {"bound": "mfma", "achieved": alg["up_flops"] / (up_ms * 1e-3) / 1e12,
-                "peak": MFMA_PEAK_TFLOPS[wl.w_dtype], "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl.name, "up_gemm")
-    roof["kernel"] = "grouped up GEMM (W1, W3, SiLU*mul; routed + shared)"
-    roof["kernel_ms"] = up_ms
-
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    out = {
-        "metric": "MoE-layer tokens/s at d=7168, 256 experts top-8; % of HBM or MFMA roofline",
-        "value": wl.T / (ms_per_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {W.F32: "f32", W.BF16: "bf16", W.FP8_E4M3: "fp8_e4m3"}[wl.w_dtype],
-        "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "inter": wl.inter,
-                   "inter_shared": wl.inter_shared, "parallelism": "none (one GPU)"},
-        "roofline": roof,
-        "layer": {"algorithmic_GB": alg["layer_bytes"] / 1e9, "touched_experts": alg["touched"],
-                  "GB_per_s": alg["layer_bytes"] / (ms_per_step * 1e-3) / 1e9,
-                  "hbm_frac": alg["layer_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                  "TFLOP_per_s": alg["layer_flops"] / (ms_per_step * 1e-3) / 1e12,
-                  "stage_ms": {n: float(v) for n, v in zip(B.STAGE_NAMES, stage_ms)},
-                  "down_gemm_GB_per_s": alg["dn_bytes"] / (dn_ms * 1e-3) / 1e9 if dn_ms > 0 else None},
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
+        out = run_utilization(wl, inp, args, dev)
     print(json.dumps(out), flush=True)
 
 

@@ -177,6 +177,8 @@ moe_status_t moe_route_limited(const moe_shape_t* shape, const void* x, const fl
  * bitwise.  The sum of y_partial over ranks that partition the experts and the shared features is the
  * layer output up to fp32 reassociation and the rounding of each shared slice.
  * shape->inter_shared is the full shared width (it sizes the workspace; moe_workspace_size applies).
+ * events: NULL, or MOE_NUM_STAGES + 1 caller-created events recorded between the stages as in
+ * moe_forward_staged (stage 6 is the partial combine).
  */
 moe_status_t moe_forward_shard(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
                                const uint8_t* allowed, int64_t e0, int64_t e1, int64_t n_shared,
@@ -185,7 +187,7 @@ moe_status_t moe_forward_shard(const moe_shape_t* shape, const void* x, const fl
                                const void* S1, const void* S3, const void* S2,
                                const float* S1s, const float* S3s, const float* S2s,
                                float* y_partial, int32_t* idx_out, float* w_out, int32_t* counts_out,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+                               void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
 
 /*
  * Expert-utilisation monitor ("DeepSeek-V3's mixture-of-experts architecture explained", "Where the

@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
         L.moe_route_limited.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp]
         i64 = ctypes.c_int64
         L.moe_forward_shard.restype = ctypes.c_int
-        L.moe_forward_shard.argtypes = [sp] + [vp] * 4 + [i64] * 3 + [vp] * 17 + [ctypes.c_size_t, vp]
+        L.moe_forward_shard.argtypes = [sp] + [vp] * 4 + [i64] * 3 + [vp] * 17 + [ctypes.c_size_t, vp, vp]
         L.moe_expert_utilization.restype = ctypes.c_int
         L.moe_expert_utilization.argtypes = [i64] + [vp] * 5
         L.moe_status_string.restype = ctypes.c_char_p
@@ -179,12 +179,13 @@ def forward_inputs(inp: dict, k: int, **kw):
 
 
 def moe_forward_shard(x, Wg, bias, k, e0, e1, W1, W3, W2, S1, S3, S2, inter, inter_shared, allowed=None,
-                      scales=None, y_partial=None, workspace=None, routing=False):
+                      scales=None, y_partial=None, workspace=None, routing=False, events=None):
     """One expert-parallel rank's fp32 partial output [T, d] (moe_forward_shard).
 
     W1, W3 [e1-e0, inter, d], W2 [e1-e0, d, inter]: the rank's experts (None when e0 == e1);
     S1, S3 [n_shared, d], S2 [d, n_shared]: its shared slice (None for none); `inter`, `inter_shared`:
-    the layer's full widths.  With routing=True returns (y_partial, dict(idx, w, counts)).
+    the layer's full widths.  With routing=True returns (y_partial, dict(idx, w, counts)).  `events`: as in
+    moe_forward (NUM_STAGES + 1 hipEvent_t handles recorded between stages).
     """
     T, d = x.shape
     E = Wg.shape[1]
@@ -208,7 +209,8 @@ def moe_forward_shard(x, Wg, bias, k, e0, e1, W1, W3, W2, S1, S3, S2, inter, int
                                  _ptr(sc.get("W2s")), _ptr(S1), _ptr(S3), _ptr(S2), _ptr(sc.get("S1s")),
                                  _ptr(sc.get("S3s")), _ptr(sc.get("S2s")), _ptr(y_partial),
                                  _ptr(r and r["idx"]), _ptr(r and r["w"]), _ptr(r and r["counts"]),
-                                 _ptr(workspace), workspace.numel(), _stream(dev))
+                                 _ptr(workspace), workspace.numel(), _stream(dev),
+                                 None if events is None else ctypes.cast(events, ctypes.c_void_p))
     if st:
         raise MoeError(st, "moe_forward_shard")
     return (y_partial, r) if routing else y_partial

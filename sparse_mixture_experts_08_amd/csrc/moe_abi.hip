@@ -255,11 +255,11 @@ extern "C" moe_status_t moe_forward_shard(const moe_shape_t* shape, const void* 
                                           const void* S3, const void* S2, const float* S1s, const float* S3s,
                                           const float* S2s, float* y_partial, int32_t* idx_out, float* w_out,
                                           int32_t* counts_out, void* workspace, size_t workspace_bytes,
-                                          hipStream_t stream)
+                                          hipStream_t stream, hipEvent_t* events)
 {
     return layer_impl(shape, x, Wg, bias, allowed, e0, e1, n_shared, W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s,
                       S2s, nullptr, y_partial, idx_out, w_out, counts_out, workspace, workspace_bytes, stream,
-                      nullptr);
+                      events);
 }
 
 extern "C" moe_status_t moe_expert_utilization(int64_t E, const int32_t* counts, float* util, int32_t* flags,

@@ -107,7 +107,8 @@ def _call_shard(shape, e0, e1, n_shared, ptrs=None, ws_bytes=1 << 30):
     # x, Wg, bias, allowed | W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s, S2s, y_partial, idx, w, counts, ws
     L = B.lib()
     p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(21)] if ptrs is None else ptrs
-    return L.moe_forward_shard(ctypes.byref(shape), *p[:4], e0, e1, n_shared, *p[4:], ctypes.c_size_t(ws_bytes), None)
+    return L.moe_forward_shard(ctypes.byref(shape), *p[:4], e0, e1, n_shared, *p[4:], ctypes.c_size_t(ws_bytes), None,
+                               None)
 
 
 def test_shard_argument_errors_are_host_side():
