@@ -3,7 +3,7 @@
  * feed-forward layer.
  *
  * The layer (per token t, x[t] a row of d activations):
- *   logits[e] = sum_i x[t][i] * Wg[i][e]  (+ bias[e])                       router, fp32
+ *   logits[e] = sum_i x[t][i] * Wg[e][i]  (+ bias[e])                       router, fp32
  *   (idx, v)  = the k largest logits, descending, equal logits -> lower e
  *   w         = softmax(v) over the k selected logits only
  *   y[t]      = sum_j w[j] * SwiGLU_{idx[j]}(x[t]) + SwiGLU_shared(x[t])
@@ -78,7 +78,8 @@ size_t moe_workspace_size(const moe_shape_t* shape);
 /*
  * Routing only: router logits, top-k, softmax and the expert-sorted permutation.
  *   x            [T, d] act_dtype
- *   Wg           [d, E] fp32 router weight (logits = x Wg)
+ *   Wg           [E, d] fp32 router weight, the gate's nn.Linear(d, E) weight (logits = x Wg^T);
+ *                16-byte aligned
  *   bias         [E] fp32 logit bias added before selection, or NULL
  *   idx    out   [T, k] int32 selected experts, descending logit, ties -> lower expert index
  *   w      out   [T, k] fp32 softmax over the k selected logits

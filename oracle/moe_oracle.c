@@ -140,7 +140,8 @@ static float act_value(int act_dtype, const void* x, int64_t i)
     return oracle_bf16_to_float(((const uint16_t*)x)[i]);
 }
 
-/* logits[t][e] = sum_i x[t][i] * Wg[i][e] as one fp32 FMA chain, i ascending, then + bias[e]. */
+/* logits[t][e] = sum_i x[t][i] * Wg[e][i] as one fp32 FMA chain, i ascending, then + bias[e].  Wg is the
+ * gate's nn.Linear(hidden, n_experts) weight, [E, d] [P1 block pseudocode: self.gate(x)]. */
 int oracle_router_logits(int64_t T, int64_t d, int64_t E, int act_dtype, const void* x,
                          const float* Wg, const float* bias, float* logits)
 {
@@ -148,7 +149,7 @@ int oracle_router_logits(int64_t T, int64_t d, int64_t E, int act_dtype, const v
     for (int64_t t = 0; t < T; t++) {
         for (int64_t e = 0; e < E; e++) {
             float acc = 0.0f;
-            for (int64_t i = 0; i < d; i++) acc = fmaf(act_value(act_dtype, x, t * d + i), Wg[i * E + e], acc);
+            for (int64_t i = 0; i < d; i++) acc = fmaf(act_value(act_dtype, x, t * d + i), Wg[e * d + i], acc);
             if (bias) acc = acc + bias[e];
             logits[t * E + e] = acc;
         }

@@ -84,8 +84,11 @@ def quantize_rows_e4m3(v: np.ndarray):
 
 
 def router_logits(x: np.ndarray, Wg: np.ndarray, bias, act_dtype: int) -> np.ndarray:
+    """fp32 logits [T, E] of x [T, d] under the gate weight Wg [E, d] (nn.Linear layout)."""
+    x = np.ascontiguousarray(x)
+    Wg = np.ascontiguousarray(Wg, dtype=np.float32)
     T, d = x.shape
-    E = Wg.shape[1]
+    E = Wg.shape[0]
     L = np.empty((T, E), np.float32)
     lib().oracle_router_logits(T, d, E, act_dtype, _p(x), _p(Wg), _p(bias), _p(L))
     return L
@@ -97,7 +100,7 @@ def route(x: np.ndarray, Wg: np.ndarray, bias, k: int, act_dtype: int) -> dict:
     Wg = np.ascontiguousarray(Wg, dtype=np.float32)
     bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     T, d = x.shape
-    E = Wg.shape[1]
+    E = Wg.shape[0]
     out = dict(logits=np.empty((T, E), np.float32), idx=np.empty((T, k), np.int32),
                w=np.empty((T, k), np.float32), counts=np.empty(E, np.int32),
                offsets=np.empty(E + 1, np.int32), sorted_slots=np.empty(T * k, np.int32),
@@ -117,7 +120,7 @@ def route_limited(x: np.ndarray, Wg: np.ndarray, bias, allowed: np.ndarray, k: i
     bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     allowed = np.ascontiguousarray(allowed, dtype=np.uint8)
     T, d = x.shape
-    E = Wg.shape[1]
+    E = Wg.shape[0]
     out = dict(logits=np.empty((T, E), np.float32), idx=np.empty((T, k), np.int32),
                w=np.empty((T, k), np.float32), counts=np.empty(E, np.int32),
                offsets=np.empty(E + 1, np.int32), sorted_slots=np.empty(T * k, np.int32),

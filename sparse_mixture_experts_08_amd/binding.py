@@ -106,7 +106,7 @@ def moe_route(x, Wg, bias, k, workspace=None, allowed=None):
 
     With `allowed` (uint8 [E] device tensor) calls moe_route_limited (device-limited routing)."""
     T, d = x.shape
-    E = Wg.shape[1]
+    E = Wg.shape[0]
     shape = make_shape(T, d, E, k, 128, 128, _act_code(x), _act_code(x))
     dev = x.device
     workspace, need = _workspace(shape, dev, workspace)
@@ -188,7 +188,7 @@ def moe_forward_shard(x, Wg, bias, k, e0, e1, W1, W3, W2, S1, S3, S2, inter, int
     moe_forward (NUM_STAGES + 1 hipEvent_t handles recorded between stages).
     """
     T, d = x.shape
-    E = Wg.shape[1]
+    E = Wg.shape[0]
     n_shared = 0 if S1 is None else S1.shape[0]
     wt = W1 if W1 is not None else S1
     shape = make_shape(T, d, E, k, inter, inter_shared, _act_code(x), _w_code(wt) if wt is not None else _act_code(x))

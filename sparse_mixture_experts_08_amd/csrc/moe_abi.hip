@@ -127,7 +127,7 @@ static moe_status_t route_impl(const moe_shape_t* shape, const void* x, const fl
     const moe_shape_t& s = *shape;
     if (s.T == 0) return MOE_OK;
     if (!x || !Wg || !idx || !w || !counts || !offsets || !sorted_slots || !workspace) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(Wg)) return MOE_ERR_INVALID_ARG;
     Workspace ws = carve_workspace(s, workspace);
     if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
     const TileRange all = {0, (int)s.E, 1};
@@ -185,7 +185,7 @@ static moe_status_t layer_impl(const moe_shape_t* shape, const void* x, const fl
     if (routed && (!W1 || !W3 || !W2 || (fp8 && (!W1s || !W3s || !W2s)))) return MOE_ERR_INVALID_ARG;
     if (with_shared && (!S1 || !S3 || !S2 || (fp8 && (!S1s || !S3s || !S2s)))) return MOE_ERR_INVALID_ARG;
     if (x == out) return MOE_ERR_INVALID_ARG;
-    const void* ptrs[] = {x, out, routed ? W1 : x, routed ? W3 : x, routed ? W2 : x, with_shared ? S1 : x,
+    const void* ptrs[] = {x, Wg, out, routed ? W1 : x, routed ? W3 : x, routed ? W2 : x, with_shared ? S1 : x,
                           with_shared ? S3 : x, with_shared ? S2 : x};
     for (const void* p : ptrs)
         if (!aligned16(p)) return MOE_ERR_INVALID_ARG;

@@ -5,9 +5,10 @@
 // logits; a softmax over those selected values only.
 //
 // Logits.  Each logit is one fp32 fused-multiply-add chain over i ascending, starting from +0.0f, then
-// one fp32 add of the optional bias.  Both kernels below are fp32 GEMMs whose K loop runs in order with
-// no split, so every (token, expert) output keeps exactly that chain and the routing decision is a
-// deterministic function of x, Wg and bias.
+// one fp32 add of the optional bias.  Wg is the gate's nn.Linear weight, [E, d]: one contiguous row per
+// expert.  Both kernels below are fp32 GEMMs whose K loop runs in order with no split, so every
+// (token, expert) output keeps exactly that chain and the routing decision is a deterministic function
+// of x, Wg and bias.
 //
 // Top-k.  One wavefront per token; each lane holds E/64 logits as 64-bit keys (order-preserving bits of
 // the logit, then the complemented expert index), so a wave-wide max picks the largest logit and, among
@@ -17,75 +18,98 @@
 
 namespace moe {
 
-// x tile element as float.
-template <typename XT> __device__ __forceinline__ float ldx(const XT* p);
-template <> __device__ __forceinline__ float ldx<float>(const float* p) { return *p; }
-template <> __device__ __forceinline__ float ldx<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+// Global loads of x and Wg are kept raw (storage format, no conversion) from the load to the LDS store,
+// at clamped in-bounds addresses, and out-of-range elements are zeroed at the store with a select.
+// Converting inside a branch around the load would make the compiler wait for each load where it is
+// issued, which serialises them and defeats the prefetch.
 
-// Eight consecutive x elements (16-byte aligned for bf16, 32-byte for fp32) as floats.
-__device__ __forceinline__ void ldx8(const uint16_t* p, float* v)
-{
-    const uint4 r = *(const uint4*)p;
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+// Eight consecutive x elements (16-byte aligned for bf16, 32-byte for fp32).
+template <typename XT> struct X8;
+template <> struct X8<uint16_t> {
+    uint4 r;
+    __device__ __forceinline__ void load(const uint16_t* p) { r = *(const uint4*)p; }
+    __device__ __forceinline__ void get(float* v, bool valid) const
+    {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        v[2 * j] = __uint_as_float(w[j] << 16);
-        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        for (int j = 0; j < 4; j++) {
+            v[2 * j] = valid ? __uint_as_float(w[j] << 16) : 0.f;
+            v[2 * j + 1] = valid ? __uint_as_float(w[j] & 0xFFFF0000u) : 0.f;
+        }
     }
-}
-__device__ __forceinline__ void ldx8(const float* p, float* v)
-{
-    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
+};
+template <> struct X8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p)
+    {
+        a = *(const float4*)p;
+        b = *(const float4*)(p + 4);
+    }
+    __device__ __forceinline__ void get(float* v, bool valid) const
+    {
+        v[0] = valid ? a.x : 0.f; v[1] = valid ? a.y : 0.f; v[2] = valid ? a.z : 0.f; v[3] = valid ? a.w : 0.f;
+        v[4] = valid ? b.x : 0.f; v[5] = valid ? b.y : 0.f; v[6] = valid ? b.z : 0.f; v[7] = valid ? b.w : 0.f;
+    }
+};
 
-// Many tokens: L[t][e] = fma chain over i of x[t][i] * Wg[i][e] (+ bias[e]).  Block tile 64 tokens x
+// Four consecutive elements of one gate row (Wg is [E, d], the gate's nn.Linear weight; rows 16-byte
+// aligned).  Rows past E are clamped to the last row and zeroed at get().
+struct W4 {
+    float4 r;
+    __device__ __forceinline__ void load(const float* Wg, int e, int i, int E, int d)
+    {
+        r = *(const float4*)(Wg + (size_t)min(e, E - 1) * d + i);
+    }
+    __device__ __forceinline__ float4 get(bool valid) const
+    {
+        return make_float4(valid ? r.x : 0.f, valid ? r.y : 0.f, valid ? r.z : 0.f, valid ? r.w : 0.f);
+    }
+};
+
+// Many tokens: L[t][e] = fma chain over i of x[t][i] * Wg[e][i] (+ bias[e]).  Block tile 64 tokens x
 // 64 experts, thread tile 4 x 4, K staged through double-buffered LDS 32 at a time (the next stage's
-// global loads are in flight during the current stage's FMAs).  x is stored transposed ([i][t]) with
-// consecutive lanes on consecutive tokens, so the transposing stores and the 16-byte reads are free of
-// bank conflicts.  Per output the K loop runs in order: the chain is exactly the contract's.
+// global loads are in flight during the current stage's FMAs).  Both tiles are stored K-major ([i][t],
+// [i][e]) so a thread reads four tokens and four experts of one i with two 16-byte reads; the x
+// transposing stores put consecutive lanes on consecutive tokens (conflict-free) and the Wg rows are
+// padded so its transposing stores spread over the banks.  Per output the K loop runs in order: the
+// chain is exactly the contract's.
 template <typename XT>
 __global__ __launch_bounds__(256) void router_logits_many_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
                                                                  const float* __restrict__ bias, float* __restrict__ L,
-                                                                 int T, int d, int E, int vec)
+                                                                 int T, int d, int E)
 {
-    constexpr int BT = 64, BE = 64, BK = 32;
+    constexpr int BT = 64, BE = 64, BK = 32, WPAD = 4;
     __shared__ __attribute__((aligned(16))) float xs[2][BK][BT];
-    __shared__ __attribute__((aligned(16))) float wsm[2][BK][BE];
+    __shared__ __attribute__((aligned(16))) float wsm[2][BK][BE + WPAD];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int e0 = blockIdx.x * BE, t0 = blockIdx.y * BT;
-    // loader roles: x -> token (tid & 63), 8 consecutive i at (tid >> 6) * 8; Wg -> rows tid / 16 and
-    // tid / 16 + 16, 4 experts at (tid & 15) * 4
+    // loader roles: x -> token (tid & 63), 8 consecutive i at (tid >> 6) * 8; Wg -> experts tid / 8 and
+    // tid / 8 + 32, 4 consecutive i at (tid & 7) * 4
     const int lx_t = tid & 63, lx_k = (tid >> 6) * 8;
-    const int lw_k = tid >> 4, lw_c = (tid & 15) * 4;
-    float xr[8];
-    float4 wr[2];
+    const int lw_e = tid >> 3, lw_k = (tid & 7) * 4;
+    const bool x_ok = t0 + lx_t < T;
+    const XT* xrow = x + (size_t)min(t0 + lx_t, T - 1) * d + lx_k;
+    X8<XT> xr;
+    W4 wr[2];
     auto load = [&](int k0) {
-        if (t0 + lx_t < T) {
-            ldx8(x + (size_t)(t0 + lx_t) * d + k0 + lx_k, xr);
-        } else {
+        xr.load(xrow + k0);
 #pragma unroll
-            for (int j = 0; j < 8; j++) xr[j] = 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const float* row = Wg + (size_t)(k0 + lw_k + 16 * h) * E + e0 + lw_c;
-            if (vec && e0 + lw_c + 4 <= E) {
-                wr[h] = *(const float4*)row;
-            } else {
-                wr[h].x = e0 + lw_c + 0 < E ? row[0] : 0.f;
-                wr[h].y = e0 + lw_c + 1 < E ? row[1] : 0.f;
-                wr[h].z = e0 + lw_c + 2 < E ? row[2] : 0.f;
-                wr[h].w = e0 + lw_c + 3 < E ? row[3] : 0.f;
-            }
-        }
+        for (int h = 0; h < 2; h++) wr[h].load(Wg, e0 + lw_e + 32 * h, k0 + lw_k, E, d);
     };
     auto store = [&](int b) {
+        float v[8];
+        xr.get(v, x_ok);
 #pragma unroll
-        for (int j = 0; j < 8; j++) xs[b][lx_k + j][lx_t] = xr[j];
+        for (int j = 0; j < 8; j++) xs[b][lx_k + j][lx_t] = v[j];
 #pragma unroll
-        for (int h = 0; h < 2; h++) *(float4*)&wsm[b][lw_k + 16 * h][lw_c] = wr[h];
+        for (int h = 0; h < 2; h++) {
+            const int e = lw_e + 32 * h;
+            const float4 w = wr[h].get(e0 + e < E);
+            wsm[b][lw_k + 0][e] = w.x;
+            wsm[b][lw_k + 1][e] = w.y;
+            wsm[b][lw_k + 2][e] = w.z;
+            wsm[b][lw_k + 3][e] = w.w;
+        }
     };
 
     float acc[4][4];
@@ -130,57 +154,40 @@ __global__ __launch_bounds__(256) void router_logits_many_kernel(const XT* __res
 }
 
 // Few tokens: one chain per lane.  Block = 16 tokens x 16 experts, 4 wavefronts (wave w: tokens
-// 4w..4w+3; lane (tt, el) = (lane / 16, lane % 16)).  Per 128-wide K stage the block loads the Wg tile
-// [128 i][16 e] (64-byte row segments) and the x tile [16 t][128 i] and stores them in LDS transposed
-// ([e][i], [t][i]) so each lane reads four consecutive i of its expert and of its token with one 16-byte
-// LDS read.  Global loads run two stages ahead of the FMAs (two register sets, loop unrolled by two).
+// 4w..4w+3; lane (tt, el) = (lane / 16, lane % 16)).  Per 128-wide K stage the block copies the Wg
+// tile (16 gate rows, 512 bytes each) and the x tile (16 token rows) into LDS as [e][i] and [t][i], so
+// each lane reads four consecutive i of its expert and of its token with one 16-byte read.  Global
+// loads run two stages ahead of the FMAs (two register sets, loop unrolled by two).
 template <typename XT>
 __global__ __launch_bounds__(256) void router_logits_few_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
                                                                 const float* __restrict__ bias, float* __restrict__ L,
-                                                                int T, int d, int E, int vec)
+                                                                int T, int d, int E)
 {
     constexpr int BK = 128, PAD = 4;
     __shared__ __attribute__((aligned(16))) float wT[2][16][BK + PAD];
     __shared__ __attribute__((aligned(16))) float xT[2][16][BK + PAD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tt = wave * 4 + (lane >> 4), el = lane & 15;
     const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
-    const int wr_row = tid >> 1, wr_col = (tid & 1) * 8;       // Wg tile element loaded by this thread
-    const int xr_tok = tid >> 4, xr_i = (tid & 15) * 8;        // x tile element loaded by this thread
+    const int lr = tid >> 4, li = (tid & 15) * 8;              // row (expert / token) and first i loaded
+    const bool w_ok = e0 + lr < E, x_ok = t0 + lr < T;
+    const XT* xrow = x + (size_t)min(t0 + lr, T - 1) * d + li;
 
     struct Regs {
-        float4 w0, w1;
-        float x[8];
+        W4 w0, w1;
+        X8<XT> x;
     };
     auto load = [&](Regs& r, int k0) {
-        const float* row = Wg + (size_t)(k0 + wr_row) * E + e0 + wr_col;
-        if (vec) {
-            r.w0 = *(const float4*)row;
-            r.w1 = *(const float4*)(row + 4);
-        } else {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) v[j] = e0 + wr_col + j < E ? row[j] : 0.f;
-            r.w0 = make_float4(v[0], v[1], v[2], v[3]);
-            r.w1 = make_float4(v[4], v[5], v[6], v[7]);
-        }
-        if (t0 + xr_tok < T) {
-            ldx8(x + (size_t)(t0 + xr_tok) * d + k0 + xr_i, r.x);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; j++) r.x[j] = 0.f;
-        }
+        r.w0.load(Wg, e0 + lr, k0 + li, E, d);
+        r.w1.load(Wg, e0 + lr, k0 + li + 4, E, d);
+        r.x.load(xrow + k0);
     };
     auto store = [&](const Regs& r, int b) {
-        wT[b][wr_col + 0][wr_row] = r.w0.x;
-        wT[b][wr_col + 1][wr_row] = r.w0.y;
-        wT[b][wr_col + 2][wr_row] = r.w0.z;
-        wT[b][wr_col + 3][wr_row] = r.w0.w;
-        wT[b][wr_col + 4][wr_row] = r.w1.x;
-        wT[b][wr_col + 5][wr_row] = r.w1.y;
-        wT[b][wr_col + 6][wr_row] = r.w1.z;
-        wT[b][wr_col + 7][wr_row] = r.w1.w;
-        *(float4*)&xT[b][xr_tok][xr_i] = make_float4(r.x[0], r.x[1], r.x[2], r.x[3]);
-        *(float4*)&xT[b][xr_tok][xr_i + 4] = make_float4(r.x[4], r.x[5], r.x[6], r.x[7]);
+        *(float4*)&wT[b][lr][li] = r.w0.get(w_ok);
+        *(float4*)&wT[b][lr][li + 4] = r.w1.get(w_ok);
+        float v[8];
+        r.x.get(v, x_ok);
+        *(float4*)&xT[b][lr][li] = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)&xT[b][lr][li + 4] = make_float4(v[4], v[5], v[6], v[7]);
     };
     float acc = 0.0f;
     auto compute = [&](int b) {
@@ -221,25 +228,27 @@ __global__ __launch_bounds__(256) void router_logits_few_kernel(const XT* __rest
     }
 }
 
+#ifndef MOE_ROUTER_FEW_MAX_T
+#define MOE_ROUTER_FEW_MAX_T 512
+#endif
+
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
                                 float* logits, hipStream_t stream)
 {
     const int T = (int)s.T, d = (int)s.d, E = (int)s.E;
     const bool bf = s.act_dtype == MOE_BF16;
-    if (T <= 512) {
-        const int vec = (E % 16 == 0) && (((uintptr_t)Wg & 15) == 0);
+    if (T <= MOE_ROUTER_FEW_MAX_T) {
         dim3 grid((E + 15) / 16, (T + 15) / 16);
         if (bf)
-            router_logits_few_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E, vec);
+            router_logits_few_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_few_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E, vec);
+            router_logits_few_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     } else {
-        const int vec = (E % 4 == 0) && (((uintptr_t)Wg & 15) == 0);
         dim3 grid((E + 63) / 64, (T + 63) / 64);
         if (bf)
-            router_logits_many_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E, vec);
+            router_logits_many_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_many_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E, vec);
+            router_logits_many_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     }
     return hipGetLastError();
 }

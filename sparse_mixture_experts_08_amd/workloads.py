@@ -116,14 +116,14 @@ def skew_bias(E: int, seed: int, device="cpu") -> torch.Tensor:
 def generate(wl: Workload, seed: int = 0, device="cpu", weights=True) -> dict:
     """All inputs of one layer invocation as torch tensors on `device`.
 
-    Keys: x [T,d]; Wg [d,E] fp32; bias [E] fp32 or None; W1, W3 [E,inter,d]; W2 [E,d,inter];
+    Keys: x [T,d]; Wg [E,d] fp32 (the gate's nn.Linear weight); bias [E] fp32 or None; W1, W3 [E,inter,d]; W2 [E,d,inter];
     S1, S3 [inter_s,d]; S2 [d,inter_s]; fp8 only: W1s, W3s [E,inter/128,d/128], W2s [E,d/128,inter/128],
     S1s, S3s [inter_s/128,d/128], S2s [d/128,inter_s/128].
     """
     act = torch.float32 if wl.act_dtype == F32 else torch.bfloat16
     out = {}
     out["x"] = _normal((wl.T, wl.d), 1.0, _gen(seed, "x", device), device).to(act)
-    out["Wg"] = _normal((wl.d, wl.E), 1.0 / math.sqrt(wl.d), _gen(seed, "Wg", device), device)
+    out["Wg"] = _normal((wl.E, wl.d), 1.0 / math.sqrt(wl.d), _gen(seed, "Wg", device), device)
     out["bias"] = skew_bias(wl.E, seed, device) if wl.skew else None
     if not weights:
         return out
@@ -149,5 +149,5 @@ def to_numpy(t):
 
 def weight_shapes(wl: Workload) -> dict:
     """Shapes of the weight tensors `generate` returns (no allocation)."""
-    return dict(Wg=(wl.d, wl.E), W1=(wl.E, wl.inter, wl.d), W3=(wl.E, wl.inter, wl.d), W2=(wl.E, wl.d, wl.inter),
+    return dict(Wg=(wl.E, wl.d), W1=(wl.E, wl.inter, wl.d), W3=(wl.E, wl.inter, wl.d), W2=(wl.E, wl.d, wl.inter),
                 S1=(wl.inter_shared, wl.d), S3=(wl.inter_shared, wl.d), S2=(wl.d, wl.inter_shared))

@@ -61,8 +61,8 @@ def test_all_tokens_to_one_expert_and_zero_count_experts():
 def test_exact_logit_ties_go_to_lower_index():
     wl = W.Workload("ties", 128, 512, 32, 4, 256, 256, BF16, BF16)
     inp = W.generate(wl, seed=3, device=DEV)
-    inp["Wg"][:, 20] = inp["Wg"][:, 3]          # experts 3 and 20 always tie
-    inp["Wg"][:, 31] = inp["Wg"][:, 30]
+    inp["Wg"][20] = inp["Wg"][3]                # experts 3 and 20 always tie
+    inp["Wg"][31] = inp["Wg"][30]
     run_parity(wl, inp)
     r = B.moe_route(inp["x"], inp["Wg"], None, wl.k)
     idx = r["idx"].cpu().numpy()

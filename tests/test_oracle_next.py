@@ -40,7 +40,7 @@ def _bf16(t):
 
 def test_limited_routing_all_allowed_equals_plain_routing(oracle):
     g = torch.Generator().manual_seed(1)
-    x, Wg = _bf16(torch.randn(70, 64, generator=g)), torch.randn(64, 24, generator=g).numpy()
+    x, Wg = _bf16(torch.randn(70, 64, generator=g)), torch.randn(24, 64, generator=g).numpy()
     a = oracle.route(x, Wg, None, 4, BF16)
     b = oracle.route_limited(x, Wg, None, np.ones(24, np.uint8), 4, BF16)
     for key in ("idx", "w", "counts", "offsets", "sorted_slots", "pos"):
@@ -50,7 +50,7 @@ def test_limited_routing_all_allowed_equals_plain_routing(oracle):
 def test_limited_routing_equals_masked_topk_and_softmax(oracle):
     g = torch.Generator().manual_seed(2)
     T, d, E, k = 90, 48, 32, 6
-    x, Wg = _bf16(torch.randn(T, d, generator=g)), torch.randn(d, E, generator=g).numpy()
+    x, Wg = _bf16(torch.randn(T, d, generator=g)), torch.randn(E, d, generator=g).numpy()
     allowed = (torch.rand(E, generator=g) < 0.4).to(torch.uint8)
     allowed[:k] = 1
     r = oracle.route_limited(x, Wg, None, allowed.numpy(), k, BF16)
@@ -69,7 +69,7 @@ def test_limited_routing_brute_force_and_too_few_allowed(oracle):
     g = torch.Generator().manual_seed(3)
     E, k = 9, 3
     x = torch.randint(-2, 3, (30, 3), generator=g).float()
-    Wg = torch.randint(-1, 2, (3, E), generator=g).float()
+    Wg = torch.randint(-1, 2, (E, 3), generator=g).float()
     allowed = np.array([1, 0, 1, 1, 0, 1, 1, 0, 1], np.uint8)
     r = oracle.route_limited(_bf16(x), Wg.numpy(), None, allowed, k, BF16)
     L = r["logits"]

@@ -22,14 +22,15 @@ def _bf16(t):
     return W.to_numpy(t.to(torch.bfloat16))
 
 
-def test_logits_one_hot_rows_pick_wg_rows(oracle):
-    # x = e_i  ->  logit[e] = Wg[i, e] exactly (catches a transposed or mis-indexed Wg)
+def test_logits_one_hot_rows_pick_wg_columns(oracle):
+    # x = e_i  ->  logit[e] = Wg[e, i] exactly (the gate's nn.Linear weight is [E, d]; catches a
+    # transposed or mis-indexed Wg)
     d, E = 48, 20
     g = torch.Generator().manual_seed(0)
-    Wg = torch.randn(d, E, generator=g)
+    Wg = torch.randn(E, d, generator=g)
     x = torch.eye(d)
     L = oracle.router_logits(x.numpy(), Wg.numpy(), None, F32)
-    assert np.array_equal(L, Wg.numpy())
+    assert np.array_equal(L, Wg.numpy().T)
 
 
 def test_logits_exact_on_small_integers(oracle):
@@ -37,9 +38,9 @@ def test_logits_exact_on_small_integers(oracle):
     T, d, E = 9, 300, 17
     g = torch.Generator().manual_seed(1)
     x = torch.randint(-8, 9, (T, d), generator=g).float()
-    Wg = torch.randint(-16, 17, (d, E), generator=g).float()
+    Wg = torch.randint(-16, 17, (E, d), generator=g).float()
     L = oracle.router_logits(_bf16(x), Wg.numpy(), None, BF16)
-    exact = x.long() @ Wg.long()
+    exact = x.long() @ Wg.long().T
     assert np.array_equal(L, exact.numpy().astype(np.float32))
 
 
@@ -49,14 +50,14 @@ def test_logits_within_fp32_chain_error_bound(oracle):
     T, d, E = 3, 257, 5
     g = torch.Generator().manual_seed(2)
     x = torch.randn(T, d, generator=g).to(torch.bfloat16)
-    Wg = torch.randn(d, E, generator=g)
+    Wg = torch.randn(E, d, generator=g)
     L = oracle.router_logits(W.to_numpy(x), Wg.numpy(), None, BF16)
     u = 2.0 ** -24
     gamma = d * u / (1 - d * u)
     xf = x.float()
     for t in range(T):
         for e in range(E):
-            prods = [Fraction(float(xf[t, i])) * Fraction(float(Wg[i, e])) for i in range(d)]
+            prods = [Fraction(float(xf[t, i])) * Fraction(float(Wg[e, i])) for i in range(d)]
             exact = sum(prods)
             bound = gamma * float(sum(abs(p) for p in prods))
             assert abs(Fraction(float(L[t, e])) - exact) <= Fraction(bound)
@@ -66,7 +67,7 @@ def test_logits_bias_is_one_fp32_add(oracle):
     T, d, E = 11, 64, 16
     g = torch.Generator().manual_seed(3)
     x = _bf16(torch.randn(T, d, generator=g))
-    Wg = torch.randn(d, E, generator=g).numpy()
+    Wg = torch.randn(E, d, generator=g).numpy()
     b = torch.randn(E, generator=g).numpy()
     L0 = oracle.router_logits(x, Wg, None, BF16)
     L1 = oracle.router_logits(x, Wg, b, BF16)
@@ -84,7 +85,7 @@ def test_topk_brute_force_over_subsets(oracle):
     for E, k in [(6, 1), (7, 2), (8, 3), (10, 4), (9, 9)]:
         T, d = 40, 3
         x = torch.randint(-2, 3, (T, d), generator=g).float()
-        Wg = torch.randint(-1, 2, (d, E), generator=g).float()
+        Wg = torch.randint(-1, 2, (E, d), generator=g).float()
         r = oracle.route(_bf16(x), Wg.numpy(), None, k, BF16)
         L = r["logits"]
         for t in range(T):
@@ -99,9 +100,9 @@ def test_topk_equals_stable_sort_and_duplicate_columns_tie_low_first(oracle):
     T, d, E, k = 64, 32, 24, 6
     g = torch.Generator().manual_seed(5)
     x = torch.randn(T, d, generator=g)
-    Wg = torch.randn(d, E, generator=g)
-    Wg[:, 13] = Wg[:, 4]          # duplicated columns: identical logits for experts 4 and 13
-    Wg[:, 20] = Wg[:, 19]
+    Wg = torch.randn(E, d, generator=g)
+    Wg[13] = Wg[4]                # duplicated gate rows: identical logits for experts 4 and 13
+    Wg[20] = Wg[19]
     r = oracle.route(_bf16(x), Wg.numpy(), None, k, BF16)
     L = torch.from_numpy(r["logits"])
     assert torch.equal(L[:, 4], L[:, 13])
@@ -116,7 +117,7 @@ def test_topk_equals_stable_sort_and_duplicate_columns_tie_low_first(oracle):
 def test_zero_input_routes_to_lowest_indices_with_equal_weights(oracle):
     T, d, E, k = 5, 64, 16, 4
     x = np.zeros((T, d), np.float32)
-    Wg = torch.randn(d, E, generator=torch.Generator().manual_seed(6)).numpy()
+    Wg = torch.randn(E, d, generator=torch.Generator().manual_seed(6)).numpy()
     r = oracle.route(x, Wg, None, k, F32)
     assert (r["idx"] == np.arange(k)).all()
     assert (r["w"] == np.float32(1.0 / k)).all()
@@ -125,7 +126,7 @@ def test_zero_input_routes_to_lowest_indices_with_equal_weights(oracle):
 def test_softmax_closed_forms(oracle):
     g = torch.Generator().manual_seed(7)
     x = _bf16(torch.randn(50, 40, generator=g))
-    Wg = torch.randn(40, 12, generator=g).numpy()
+    Wg = torch.randn(12, 40, generator=g).numpy()
     r1 = oracle.route(x, Wg, None, 1, BF16)
     assert (r1["w"] == 1.0).all()                                      # k = 1: weight exactly 1
     r2 = oracle.route(x, Wg, None, 2, BF16)
@@ -141,7 +142,7 @@ def test_routing_invariants_and_reference_calls(oracle):
     T, d, E, k = 300, 96, 32, 5
     g = torch.Generator().manual_seed(8)
     x = _bf16(torch.randn(T, d, generator=g))
-    Wg = (torch.randn(d, E, generator=g) / math.sqrt(d)).numpy()
+    Wg = (torch.randn(E, d, generator=g) / math.sqrt(d)).numpy()
     r = oracle.route(x, Wg, None, k, BF16)
     idx = torch.from_numpy(r["idx"]).long()
     w = r["w"]
@@ -166,7 +167,7 @@ def test_token_permutation_equivariance(oracle):
     T, d, E, k = 64, 80, 16, 3
     g = torch.Generator().manual_seed(9)
     x = torch.randn(T, d, generator=g)
-    Wg = torch.randn(d, E, generator=g).numpy()
+    Wg = torch.randn(E, d, generator=g).numpy()
     perm = torch.randperm(T, generator=g)
     r = oracle.route(_bf16(x), Wg, None, k, BF16)
     rp = oracle.route(_bf16(x[perm]), Wg, None, k, BF16)
