@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
         ww[b + 1] = v;
     }
     const int64_t shared_row = (int64_t)T * k + t;
-    for (int c = threadIdx.x * VE; c < d; c += 256 * VE) {
+    // block (t, column chunk): 256 threads x one 16-byte vector each
+    for (int c = (blockIdx.y * 256 + threadIdx.x) * VE; c < d; c += gridDim.y * 256 * VE) {
         float acc[VE];
 #pragma unroll
         for (int e = 0; e < VE; e++) acc[e] = 0.0f;
@@ -71,14 +72,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
 }
 
+// Grid: with few tokens one block per (token, 256 vectors of the row), so decode-sized T still spreads
+// over the CUs; with many tokens one block per token, which amortises the slot sort over the row.
+static dim3 combine_grid(const moe_shape_t& s)
+{
+    const int ve = s.act_dtype == MOE_BF16 ? 8 : 4;
+    return dim3((unsigned)s.T, s.T >= 1024 ? 1u : (unsigned)((s.d + 256 * ve - 1) / (256 * ve)));
+}
+
 hipError_t launch_combine(const moe_shape_t& s, const int32_t* pos, const float* w, const Workspace& ws, void* y,
                           hipStream_t stream)
 {
     if (s.act_dtype == MOE_BF16)
-        combine_kernel<true><<<(unsigned)s.T, 256, 0, stream>>>(pos, w, (const uint8_t*)ws.y_rows, (int)s.T, (int)s.d,
+        combine_kernel<true><<<combine_grid(s), 256, 0, stream>>>(pos, w, (const uint8_t*)ws.y_rows, (int)s.T, (int)s.d,
                                                                 (int)s.k, (uint8_t*)y);
     else
-        combine_kernel<false><<<(unsigned)s.T, 256, 0, stream>>>(pos, w, (const uint8_t*)ws.y_rows, (int)s.T, (int)s.d,
+        combine_kernel<false><<<combine_grid(s), 256, 0, stream>>>(pos, w, (const uint8_t*)ws.y_rows, (int)s.T, (int)s.d,
                                                                  (int)s.k, (uint8_t*)y);
     return hipGetLastError();
 }
@@ -119,7 +128,8 @@ __global__ __launch_bounds__(256) void combine_partial_kernel(const int32_t* __r
         ww[b + 1] = v;
     }
     const int64_t shared_row = (int64_t)T * k + t;
-    for (int c = threadIdx.x * VE; c < d; c += 256 * VE) {
+    // block (t, column chunk): 256 threads x one 16-byte vector each
+    for (int c = (blockIdx.y * 256 + threadIdx.x) * VE; c < d; c += gridDim.y * 256 * VE) {
         float acc[VE];
 #pragma unroll
         for (int e = 0; e < VE; e++) acc[e] = 0.0f;
@@ -156,10 +166,10 @@ hipError_t launch_combine_partial(const moe_shape_t& s, const int32_t* idx, cons
                                   hipStream_t stream)
 {
     if (s.act_dtype == MOE_BF16)
-        combine_partial_kernel<true><<<(unsigned)s.T, 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
+        combine_partial_kernel<true><<<combine_grid(s), 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
                                                                         (int)s.d, (int)s.k, e0, e1, with_shared, y_partial);
     else
-        combine_partial_kernel<false><<<(unsigned)s.T, 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
+        combine_partial_kernel<false><<<combine_grid(s), 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
                                                                          (int)s.d, (int)s.k, e0, e1, with_shared, y_partial);
     return hipGetLastError();
 }

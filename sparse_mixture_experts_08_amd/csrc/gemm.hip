@@ -57,6 +57,7 @@ struct GemmArgs {
     int64_t ld_s;             // elements between shared weight rows (a slice of a wider expert)
     int nkb_s;                // fp8: scale blocks between shared scale rows
     int max_tiles;
+    int krot;                 // K-stage rotation per n-block (0: every block walks K from stage 0)
     int group_m;              // 0: block b -> (tile b / n_blocks, n-block b % n_blocks); else the XCD-aware
                               // grouped order below, with group_m tiles per group
 };
@@ -251,7 +252,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
         }
     }
     i32x4 reg[PER];
-    auto load_stage = [&](int s) {
+    // K-stage order: rotated by the n-block, so blocks streaming weight rows at the same time read
+    // different column offsets of them and spread over the HBM channels.  (The fp32 sum over K stages
+    // then runs in a rotated but fixed order per output column: still deterministic.)
+    const int nstages = K / KE;
+    const int kshift = (nb * g.krot) % nstages;
+    auto kst = [&](int s) { return s + kshift >= nstages ? s + kshift - nstages : s + kshift; };
+    auto load_stage = [&](int s0) {
+        const int s = kst(s0);
 #pragma unroll
         for (int p = 0; p < PER; p++) {
             reg[p] = (i32x4){0, 0, 0, 0};
@@ -278,25 +286,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
 #pragma unroll
         for (int j = 0; j < WN; j++) acc1[i][j] = acc3[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    const int nstages = K / KE;
     load_stage(0);
     store_stage(0);
-    load_scales(0, 0);
+    load_scales(kst(0), 0);
     __syncthreads();
     for (int s = 0; s < nstages; s++) {
         const int buf = NBUF == 2 ? (s & 1) : 0;
         if (s + 1 < nstages) load_stage(s + 1);
         float sb1 = 0.f, sb3 = 0.f;
         if constexpr (FP8) {
-            sb1 = W1s[s];
-            if constexpr (UP) sb3 = W3s[s];
+            sb1 = W1s[kst(s)];
+            if constexpr (UP) sb3 = W3s[kst(s)];
         }
         mma_stage<ET, UP, WM, WN, BN>(smem + buf * ROWS * 128, smem + buf * ROWS * 128 + BM * 128, sA[buf], sb1, sb3,
                                       wm0, wn0, lane, acc1, acc3);
         if constexpr (NBUF == 1) __syncthreads();
         if (s + 1 < nstages) {
             store_stage(NBUF == 2 ? buf ^ 1 : 0);
-            load_scales(s + 1, NBUF == 2 ? buf ^ 1 : 0);
+            load_scales(kst(s + 1), NBUF == 2 ? buf ^ 1 : 0);
         }
         __syncthreads();
     }
@@ -450,6 +457,40 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 #define MOE_BIG_DN_BN 256
 #endif
 
+// 16-row tiles, up GEMM (bf16): output features (of W1 and of W3) per block, wavefronts, minimum
+// wavefronts per SIMD.  inter and inter_shared must be multiples of MOE_SMALL_UP_BN.
+#ifndef MOE_SMALL_UP_BN
+#define MOE_SMALL_UP_BN 64
+#endif
+#ifndef MOE_SMALL_UP_WAVES
+#define MOE_SMALL_UP_WAVES 4
+#endif
+#ifndef MOE_SMALL_UP_MINW
+#define MOE_SMALL_UP_MINW 1
+#endif
+// 16-row tiles, down GEMM (bf16): output features per block, wavefronts, minimum wavefronts per SIMD.
+#ifndef MOE_SMALL_DN_BN
+#define MOE_SMALL_DN_BN 64
+#endif
+#ifndef MOE_SMALL_DN_WAVES
+#define MOE_SMALL_DN_WAVES 4
+#endif
+#ifndef MOE_SMALL_DN_MINW
+#define MOE_SMALL_DN_MINW 1
+#endif
+
+// K-stage rotation per n-block: the down GEMM (rows of inter elements) and the up GEMM with 128-row
+// tiles gain from it; the up GEMM with 16-row tiles already streams at the HBM ceiling without it.
+#ifndef MOE_KROT_UP16
+#define MOE_KROT_UP16 0
+#endif
+#ifndef MOE_KROT_UP
+#define MOE_KROT_UP 3
+#endif
+#ifndef MOE_KROT_DN
+#define MOE_KROT_DN 1
+#endif
+
 // Common fields of both GEMMs' arguments.
 static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws, int e_base)
 {
@@ -494,6 +535,7 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     up.N_s = n_shared;
     up.K_r = up.K_s = (int)s.d;
     const int bm = tile_rows(s);
+    up.krot = bm == 16 ? MOE_KROT_UP16 : MOE_KROT_UP;
     if (fp8) {
         up.n_blocks = (int)(ws.inter_max / 128);
         if (bm == 16) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
@@ -504,8 +546,8 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
         else launch_one<ET_F32, true, false, 128, 64, 2, 2>(up, stream);
     } else {
         if (bm == 16) {
-            up.n_blocks = (int)(ws.inter_max / 64);
-            launch_one<ET_BF16, true, true, 16, 64, 1, 4>(up, stream);
+            up.n_blocks = (int)(ws.inter_max / MOE_SMALL_UP_BN);
+            launch_one<ET_BF16, true, true, 16, MOE_SMALL_UP_BN, 1, MOE_SMALL_UP_WAVES, 2, MOE_SMALL_UP_MINW>(up, stream);
         } else if (bm == 128) {
             up.n_blocks = (int)(ws.inter_max / MOE_MID_UP_BN);
             launch_one<ET_BF16, true, true, 128, MOE_MID_UP_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(up, stream);
@@ -539,12 +581,16 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     dn.N_r = dn.N_s = (int)s.d;
     dn.K_r = (int)s.inter;
     dn.K_s = n_shared;
+    dn.krot = MOE_KROT_DN;
     const int bm = tile_rows(s);
     if (bm == 16) {
         dn.n_blocks = (int)(s.d / 64);
         if (fp8) launch_one<ET_FP8, false, true, 16, 64, 1, 4>(dn, stream);
         else if (f32) launch_one<ET_F32, false, false, 16, 64, 1, 4>(dn, stream);
-        else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
+        else if (s.d % MOE_SMALL_DN_BN == 0) {
+            dn.n_blocks = (int)(s.d / MOE_SMALL_DN_BN);
+            launch_one<ET_BF16, false, true, 16, MOE_SMALL_DN_BN, 1, MOE_SMALL_DN_WAVES, 2, MOE_SMALL_DN_MINW>(dn, stream);
+        } else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
     } else if (s.d % 256) {
         // d an odd multiple of 128: 128-wide n-blocks (the wider configurations need d % 256 == 0)
         dn.n_blocks = (int)(s.d / 128);
