@@ -45,6 +45,8 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int k,
 // ---------------------------------------------------------------------------------------------------
 // Fused path (T <= 256): one block of 1024 threads.
 // ---------------------------------------------------------------------------------------------------
+// SMALL_E: E <= 256 (16 lanes per token); otherwise a wavefront per token (E <= 1024).
+template <bool SMALL_E>
 __global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restrict__ L, const uint8_t* __restrict__ allowed,
                                                            int T, int E, int k, int bm, TileRange tr,
                                                            int32_t* __restrict__ idx, float* __restrict__ w,
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restri
     __syncthreads();
 
     // top-k: 16 lanes per token when E <= 256, else a whole wavefront per token
-    if (E <= 256) {
+    if constexpr (SMALL_E) {
         const int g = lane >> 4, sub = lane & 15;
         for (int t0 = wave * 4; t0 < T; t0 += 64) {
             const int t = t0 + g;
@@ -214,8 +216,12 @@ hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, const
                                 int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos,
                                 const Workspace& ws, int bm, TileRange tr, hipStream_t stream)
 {
-    route_fused_kernel<<<1, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, bm, tr, idx, w, counts, offsets,
-                                               sorted_slots, pos, ws.row_token, ws.tiles, ws.sync);
+    if (s.E <= 256)
+        route_fused_kernel<true><<<1, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, bm, tr, idx, w, counts,
+                                                         offsets, sorted_slots, pos, ws.row_token, ws.tiles, ws.sync);
+    else
+        route_fused_kernel<false><<<1, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, bm, tr, idx, w, counts,
+                                                          offsets, sorted_slots, pos, ws.row_token, ws.tiles, ws.sync);
     return hipGetLastError();
 }
 

@@ -153,41 +153,51 @@ __global__ __launch_bounds__(256) void router_logits_many_kernel(const XT* __res
     }
 }
 
-// Few tokens: one chain per lane.  Block = 16 tokens x 16 experts, 4 wavefronts (wave w: tokens
-// 4w..4w+3; lane (tt, el) = (lane / 16, lane % 16)).  Per 128-wide K stage the block copies the Wg
-// tile (16 gate rows, 512 bytes each) and the x tile (16 token rows) into LDS as [e][i] and [t][i], so
-// each lane reads four consecutive i of its expert and of its token with one 16-byte read.  Global
-// loads run two stages ahead of the FMAs (two register sets, loop unrolled by two).
-template <typename XT>
-__global__ __launch_bounds__(256) void router_logits_few_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
-                                                                const float* __restrict__ bias, float* __restrict__ L,
-                                                                int T, int d, int E)
+// Few tokens: one chain per lane.  Block = TPB tokens x 16 experts, TPB / 4 wavefronts (lane (tt, el)
+// = (thread / 16, thread % 16)).  Per 128-wide K stage the block copies the Wg tile (16 gate rows, 512
+// bytes each) and the x tile (TPB token rows) into LDS as [e][i] and [t][i], so each lane reads four
+// consecutive i of its expert and of its token with one 16-byte read.  Global loads run two stages
+// ahead of the FMAs (two register sets, loop unrolled by two).
+template <typename XT, int TPB>
+__global__ __launch_bounds__(TPB * 16) void router_logits_few_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
+                                                                     const float* __restrict__ bias, float* __restrict__ L,
+                                                                     int T, int d, int E)
 {
-    constexpr int BK = 128, PAD = 4;
+    constexpr int BK = 128, PAD = 4, NT = TPB * 16;
+    constexpr int WPT = 16 * 16 / NT;                          // 8-float Wg chunks per thread
+    static_assert(TPB % 4 == 0 && TPB <= 16, "whole wavefronts, at most 16 tokens");
     __shared__ __attribute__((aligned(16))) float wT[2][16][BK + PAD];
-    __shared__ __attribute__((aligned(16))) float xT[2][16][BK + PAD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tt = wave * 4 + (lane >> 4), el = lane & 15;
-    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
-    const int lr = tid >> 4, li = (tid & 15) * 8;              // row (expert / token) and first i loaded
-    const bool w_ok = e0 + lr < E, x_ok = t0 + lr < T;
-    const XT* xrow = x + (size_t)min(t0 + lr, T - 1) * d + li;
+    __shared__ __attribute__((aligned(16))) float xT[2][TPB][BK + PAD];
+    const int tid = threadIdx.x, tt = tid >> 4, el = tid & 15;
+    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * TPB;
+    const int li = (tid & 15) * 8;                             // first i of this thread's chunks
+    const bool x_ok = t0 + tt < T;
+    const XT* xrow = x + (size_t)min(t0 + tt, T - 1) * d + li;
 
     struct Regs {
-        W4 w0, w1;
+        W4 w[WPT][2];
         X8<XT> x;
     };
     auto load = [&](Regs& r, int k0) {
-        r.w0.load(Wg, e0 + lr, k0 + li, E, d);
-        r.w1.load(Wg, e0 + lr, k0 + li + 4, E, d);
+#pragma unroll
+        for (int p = 0; p < WPT; p++) {
+            const int e = (tid >> 4) + p * TPB;
+            r.w[p][0].load(Wg, e0 + e, k0 + li, E, d);
+            r.w[p][1].load(Wg, e0 + e, k0 + li + 4, E, d);
+        }
         r.x.load(xrow + k0);
     };
     auto store = [&](const Regs& r, int b) {
-        *(float4*)&wT[b][lr][li] = r.w0.get(w_ok);
-        *(float4*)&wT[b][lr][li + 4] = r.w1.get(w_ok);
+#pragma unroll
+        for (int p = 0; p < WPT; p++) {
+            const int e = (tid >> 4) + p * TPB;
+            *(float4*)&wT[b][e][li] = r.w[p][0].get(e0 + e < E);
+            *(float4*)&wT[b][e][li + 4] = r.w[p][1].get(e0 + e < E);
+        }
         float v[8];
         r.x.get(v, x_ok);
-        *(float4*)&xT[b][lr][li] = make_float4(v[0], v[1], v[2], v[3]);
-        *(float4*)&xT[b][lr][li + 4] = make_float4(v[4], v[5], v[6], v[7]);
+        *(float4*)&xT[b][tt][li] = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)&xT[b][tt][li + 4] = make_float4(v[4], v[5], v[6], v[7]);
     };
     float acc = 0.0f;
     auto compute = [&](int b) {
@@ -237,12 +247,19 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
 {
     const int T = (int)s.T, d = (int)s.d, E = (int)s.E;
     const bool bf = s.act_dtype == MOE_BF16;
-    if (T <= MOE_ROUTER_FEW_MAX_T) {
+    if (T <= 256) {
+        // 8 tokens per block: twice the blocks of the 16-token form, more loads in flight per token
+        dim3 grid((E + 15) / 16, (T + 7) / 8);
+        if (bf)
+            router_logits_few_kernel<uint16_t, 8><<<grid, 128, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+        else
+            router_logits_few_kernel<float, 8><<<grid, 128, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+    } else if (T <= MOE_ROUTER_FEW_MAX_T) {
         dim3 grid((E + 15) / 16, (T + 15) / 16);
         if (bf)
-            router_logits_few_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            router_logits_few_kernel<uint16_t, 16><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_few_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            router_logits_few_kernel<float, 16><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     } else {
         dim3 grid((E + 63) / 64, (T + 63) / 64);
         if (bf)
@@ -257,6 +274,8 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
 // Top-k + softmax for many tokens: one wavefront per token, 64 tokens (one chunk) per block of 16
 // wavefronts.  Also records, per chunk, which tokens chose each expert (a 64-bit mask) and how many.
 // ------------------------------------------------------------------------------------------------
+// NQ: logits per lane (E <= 64 * NQ).
+template <int NQ>
 __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restrict__ L, const uint8_t* __restrict__ allowed,
                                                             int T, int E, int k,
                                                             int32_t* __restrict__ idx, float* __restrict__ w,
@@ -274,7 +293,7 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
         if (t >= T) break;
         int my_e;
         float my_w;
-        topk_group<64, 16>(L + (size_t)t * E, allowed, E, k, lane, my_e, my_w);
+        topk_group<64, NQ>(L + (size_t)t * E, allowed, E, k, lane, my_e, my_w);
         if (lane < k) {
             idx[(size_t)t * k + lane] = my_e;
             w[(size_t)t * k + lane] = my_w;
@@ -293,8 +312,12 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
 hipError_t launch_topk(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
                        const Workspace& ws, hipStream_t stream)
 {
-    topk_softmax_kernel<<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, idx, w,
-                                                                     ws.chunk_bits, ws.chunk_counts, ws.sync);
+    if (s.E <= 256)
+        topk_softmax_kernel<4><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, idx,
+                                                                            w, ws.chunk_bits, ws.chunk_counts, ws.sync);
+    else
+        topk_softmax_kernel<16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, idx,
+                                                                             w, ws.chunk_bits, ws.chunk_counts, ws.sync);
     return hipGetLastError();
 }
 

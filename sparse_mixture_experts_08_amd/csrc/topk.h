@@ -41,11 +41,11 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t v)
     return v;
 }
 
-// The logit of expert e after the optional device-limited routing mask: -inf where allowed[e] == 0
-// (the page's `logits + mask` with mask -inf outside the allowed experts, 0 inside).
-__device__ __forceinline__ float masked_logit(const float* __restrict__ Lrow, const uint8_t* __restrict__ allowed, int e)
+// Inverse of ordered_bits (-0 comes back as +0, which compares and subtracts the same).
+__device__ __forceinline__ float key_logit(uint64_t key)
 {
-    return (allowed && !allowed[e]) ? -INFINITY : Lrow[e];
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
 // Top-k of row L[0..E) held by a group of W lanes (sub = lane index in the group), each lane holding the
@@ -55,11 +55,23 @@ template <int W, int NQ>
 __device__ __forceinline__ void topk_group(const float* __restrict__ Lrow, const uint8_t* __restrict__ allowed, int E,
                                            int k, int sub, int& my_e, float& my_w)
 {
+    // All loads first, at clamped in-bounds indices, so they are in flight together; then the keys.
+    // The device-limited routing mask (allowed[e] == 0) makes the logit -inf: the page's `logits + mask`
+    // with mask -inf outside the allowed experts and 0 inside.
+    float lv[NQ];
+    uint8_t av[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; q++) lv[q] = Lrow[min(sub + W * q, E - 1)];
+    if (allowed) {
+#pragma unroll
+        for (int q = 0; q < NQ; q++) av[q] = allowed[min(sub + W * q, E - 1)];
+    }
     uint64_t key[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; q++) {
         const int e = sub + W * q;
-        key[q] = e < E ? logit_key(masked_logit(Lrow, allowed, e), e) : 0ull;
+        const float l = (allowed && !av[q]) ? -INFINITY : lv[q];
+        key[q] = e < E ? logit_key(l, e) : 0ull;
     }
     my_e = 0;
     float my_l = 0.0f;
@@ -76,7 +88,7 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ Lrow, const
         }
         if (sub == j) {
             my_e = e;
-            my_l = masked_logit(Lrow, allowed, e);
+            my_l = key_logit(best);
         }
     }
     const float m = __shfl(my_l, 0, W);
