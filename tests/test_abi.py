@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
 
 
 def test_library_exports_every_declared_symbol():
-    L = ctypes.CDLL(B.LIB_PATH)
+    # RTLD_NOW: every symbol the library needs (kernel launch stubs included) must resolve at load
+    L = ctypes.CDLL(B.LIB_PATH, mode=os.RTLD_NOW)
     for name in _declared_functions():
         assert hasattr(L, name), name
 
