@@ -66,45 +66,50 @@ struct W4 {
     }
 };
 
-// Many tokens: L[t][e] = fma chain over i of x[t][i] * Wg[e][i] (+ bias[e]).  Block tile 64 tokens x
-// 64 experts, thread tile 4 x 4, K staged through double-buffered LDS 32 at a time (the next stage's
-// global loads are in flight during the current stage's FMAs).  Both tiles are stored K-major ([i][t],
+// Many tokens: L[t][e] = fma chain over i of x[t][i] * Wg[e][i] (+ bias[e]).  Block tile BT (64 or 32)
+// tokens x 64 experts, thread tile 4 x 4, K staged through double-buffered LDS 32 at a time; global
+// loads run two stages ahead of the FMAs (two register sets), so a CU with a single block still
+// covers their latency.  Both tiles are stored K-major ([i][t],
 // [i][e]) so a thread reads four tokens and four experts of one i with two 16-byte reads; the x
 // transposing stores put consecutive lanes on consecutive tokens (conflict-free) and the Wg rows are
 // padded so its transposing stores spread over the banks.  Per output the K loop runs in order: the
 // chain is exactly the contract's.
-template <typename XT>
-__global__ __launch_bounds__(256) void router_logits_many_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
-                                                                 const float* __restrict__ bias, float* __restrict__ L,
-                                                                 int T, int d, int E)
+template <typename XT, int BT>
+__global__ __launch_bounds__(BT * 4) void router_logits_many_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
+                                                                    const float* __restrict__ bias, float* __restrict__ L,
+                                                                    int T, int d, int E)
 {
-    constexpr int BT = 64, BE = 64, BK = 32, WPAD = 4;
+    constexpr int BE = 64, BK = 32, WPAD = 4, NT = BT * 4;
+    constexpr int WH = BE * BK / 4 / NT;               // float4 Wg loads per thread
+    static_assert(BT == 64 || BT == 32, "64- or 32-token tiles");
     __shared__ __attribute__((aligned(16))) float xs[2][BK][BT];
     __shared__ __attribute__((aligned(16))) float wsm[2][BK][BE + WPAD];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int e0 = blockIdx.x * BE, t0 = blockIdx.y * BT;
-    // loader roles: x -> token (tid & 63), 8 consecutive i at (tid >> 6) * 8; Wg -> experts tid / 8 and
-    // tid / 8 + 32, 4 consecutive i at (tid & 7) * 4
-    const int lx_t = tid & 63, lx_k = (tid >> 6) * 8;
+    // loader roles: x -> token tid % BT, 8 consecutive i at (tid / BT) * 8; Wg -> experts tid / 8 +
+    // (NT / 8) * h, 4 consecutive i at (tid % 8) * 4
+    const int lx_t = tid % BT, lx_k = (tid / BT) * 8;
     const int lw_e = tid >> 3, lw_k = (tid & 7) * 4;
     const bool x_ok = t0 + lx_t < T;
     const XT* xrow = x + (size_t)min(t0 + lx_t, T - 1) * d + lx_k;
-    X8<XT> xr;
-    W4 wr[2];
-    auto load = [&](int k0) {
-        xr.load(xrow + k0);
-#pragma unroll
-        for (int h = 0; h < 2; h++) wr[h].load(Wg, e0 + lw_e + 32 * h, k0 + lw_k, E, d);
+    struct Regs {
+        X8<XT> x;
+        W4 w[WH];
     };
-    auto store = [&](int b) {
+    auto load = [&](Regs& r, int k0) {
+        r.x.load(xrow + k0);
+#pragma unroll
+        for (int h = 0; h < WH; h++) r.w[h].load(Wg, e0 + lw_e + (NT / 8) * h, k0 + lw_k, E, d);
+    };
+    auto store = [&](const Regs& r, int b) {
         float v[8];
-        xr.get(v, x_ok);
+        r.x.get(v, x_ok);
 #pragma unroll
         for (int j = 0; j < 8; j++) xs[b][lx_k + j][lx_t] = v[j];
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int e = lw_e + 32 * h;
-            const float4 w = wr[h].get(e0 + e < E);
+        for (int h = 0; h < WH; h++) {
+            const int e = lw_e + (NT / 8) * h;
+            const float4 w = r.w[h].get(e0 + e < E);
             wsm[b][lw_k + 0][e] = w.x;
             wsm[b][lw_k + 1][e] = w.y;
             wsm[b][lw_k + 2][e] = w.z;
@@ -118,13 +123,7 @@ __global__ __launch_bounds__(256) void router_logits_many_kernel(const XT* __res
 #pragma unroll
         for (int c = 0; c < 4; c++) acc[r][c] = 0.0f;
 
-    const int ns = d / BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int s = 0; s < ns; s++) {
-        const int b = s & 1;
-        if (s + 1 < ns) load((s + 1) * BK);
+    auto compute = [&](int b) {
 #pragma unroll 8
         for (int kk = 0; kk < BK; kk++) {
             const float4 a = *(const float4*)&xs[b][kk][ty * 4];
@@ -135,7 +134,24 @@ __global__ __launch_bounds__(256) void router_logits_many_kernel(const XT* __res
 #pragma unroll
                 for (int c = 0; c < 4; c++) acc[r][c] = __builtin_fmaf(av[r], wv[c], acc[r][c]);
         }
-        if (s + 1 < ns) store(b ^ 1);
+    };
+    const int ns = d / BK;
+    Regs ra, rb;
+    load(ra, 0);
+    if (ns > 1) load(rb, BK);
+    store(ra, 0);
+    __syncthreads();
+    for (int s = 0; s < ns; s += 2) {
+        // stage s is in LDS buffer 0; rb holds stage s + 1 (in flight)
+        if (s + 2 < ns) load(ra, (s + 2) * BK);
+        compute(0);
+        if (s + 1 >= ns) break;
+        store(rb, 1);
+        __syncthreads();
+        // stage s + 1 is in LDS buffer 1; ra holds stage s + 2 (in flight)
+        if (s + 3 < ns) load(rb, (s + 3) * BK);
+        compute(1);
+        if (s + 2 < ns) store(ra, 0);
         __syncthreads();
     }
 #pragma unroll
@@ -241,6 +257,9 @@ __global__ __launch_bounds__(TPB * 16) void router_logits_few_kernel(const XT* _
 #ifndef MOE_ROUTER_FEW_MAX_T
 #define MOE_ROUTER_FEW_MAX_T 512
 #endif
+#ifndef MOE_ROUTER_BT32_MAX_T
+#define MOE_ROUTER_BT32_MAX_T 8192
+#endif
 
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
                                 float* logits, hipStream_t stream)
@@ -260,12 +279,19 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
             router_logits_few_kernel<uint16_t, 16><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
             router_logits_few_kernel<float, 16><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+    } else if (T <= MOE_ROUTER_BT32_MAX_T) {
+        // 32-token tiles: twice the blocks, so a few thousand tokens still put several blocks on a CU
+        dim3 grid((E + 63) / 64, (T + 31) / 32);
+        if (bf)
+            router_logits_many_kernel<uint16_t, 32><<<grid, 128, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+        else
+            router_logits_many_kernel<float, 32><<<grid, 128, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     } else {
         dim3 grid((E + 63) / 64, (T + 63) / 64);
         if (bf)
-            router_logits_many_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<uint16_t, 64><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_many_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<float, 64><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     }
     return hipGetLastError();
 }
