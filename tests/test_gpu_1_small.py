@@ -39,6 +39,11 @@ def test_small_parity(wl):
     W.Workload("T1-k8-E256-fp8", 1, 512, 256, 8, 256, 128, BF16, FP8),
     W.Workload("T63-k16-E16", 63, 256, 16, 16, 128, 128, BF16, BF16),      # k = E: every expert
     W.Workload("T65-E1", 65, 256, 1, 1, 128, 128, F32, F32),               # a single routed expert
+    W.Workload("E1024-k16-T300", 300, 256, 1024, 16, 128, 128, BF16, BF16),   # largest E and k, many-token top-k
+    W.Workload("E1024-k16-T100", 100, 256, 1024, 16, 128, 128, BF16, BF16),   # largest E and k, one-block routing
+    W.Workload("E257-k3-T700", 700, 128, 257, 3, 128, 128, BF16, BF16),       # E not a multiple of 16/64; d = 128
+    W.Workload("E257-k3-T40-f32", 40, 128, 257, 3, 128, 128, F32, F32),
+    W.Workload("d128-fp8-T600", 600, 128, 8, 2, 128, 128, BF16, FP8),         # smallest fp8 shape, 128-row tiles
 ], ids=lambda w: w.name)
 def test_edge_shapes(wl):
     inp = W.generate(wl, seed=1, device=DEV)
