@@ -173,6 +173,42 @@ def test_shard_full_size_decode_sampled():
     assert err <= TOL[(BF16, BF16)]
 
 
+@pytest.mark.parametrize("wl,rank", [(W.PREFILL_BF16, 3), (W.FP8_T32768.with_T(4096), 5)],
+                         ids=["prefill-bf16-rank3", "fp8-T4096-rank5"])
+def test_shard_full_width_large_tiles_sampled(wl, rank):
+    # d = 7168, E = 256 with 128-row tiles: rank `rank` of 8 (32 experts, 256 shared features); 32
+    # sampled tokens checked against the oracle, routing checked on all tokens
+    inp = W.generate(wl, seed=39, device=DEV)
+    e0, e1, s0, s1 = 32 * rank, 32 * (rank + 1), 256 * rank, 256 * (rank + 1)
+    part, rt = B.shard_inputs(inp, wl.k, e0, e1, s0, s1, routing=True)
+    torch.cuda.synchronize()
+    h = host(inp)
+    orc = oracle_route(wl, h)
+    assert np.array_equal(rt["idx"].cpu().numpy(), orc["idx"])
+    toks = np.linspace(0, wl.T - 1, 32).astype(np.int32)
+    sc = {n: h.get(n) for n in ("W1s", "W3s", "W2s", "S1s", "S3s", "S2s")}
+    ref = O.forward_shard(wl.shape(), h["x"], h["W1"], h["W3"], h["W2"], h["S1"], h["S3"], h["S2"], orc["idx"],
+                          orc["w"], e0, e1, s0, s1, tokens=toks, **sc)
+    err = rel_fro(part.cpu().numpy()[toks], ref)
+    say(f"[shard-large] {wl.name} rank {rank} rel_fro={err:.3e}")
+    assert err <= TOL[(wl.act_dtype, wl.w_dtype)]
+
+
+def test_limited_routing_full_size_decode():
+    # DeepSeek-V3 decode routing restricted to device 2 of 8 (experts 64..95): bit-exact on every token
+    wl = W.DECODE_BF16
+    inp = W.generate(wl, seed=40, device=DEV, weights=False)
+    allowed = torch.zeros(wl.E, dtype=torch.uint8)
+    allowed[64:96] = 1
+    r = B.moe_route_limited(inp["x"], inp["Wg"], None, allowed.to(DEV), wl.k)
+    torch.cuda.synchronize()
+    h = host(inp)
+    orc = O.route_limited(h["x"], h["Wg"], None, allowed.numpy(), wl.k, BF16)
+    check_routing(wl, r, orc)
+    idx = r["idx"].cpu()
+    assert ((idx >= 64) & (idx < 96)).all()
+
+
 # ---------------------------------------------------------------------------------------------------
 # expert utilisation
 # ---------------------------------------------------------------------------------------------------
