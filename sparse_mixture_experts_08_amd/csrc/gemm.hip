@@ -14,8 +14,9 @@
 //   down : A = h rows (already in sorted order), B = W2 rows, epilogue y_rows = round(acc).
 // Empty experts create no tiles and read no weights.
 //
-// Data path.  A and B tiles are staged through LDS in 128-byte-per-row K stages (double buffered,
-// 16-byte chunks XOR-swizzled by row), fragments read with 16-byte LDS reads.  MFMA per element type:
+// Data path.  A and B tiles are staged through LDS in 128-byte-per-row K stages (global loads into
+// registers one stage ahead; one or two LDS buffers; 16-byte chunks XOR-swizzled by row), fragments
+// read with 16-byte LDS reads.  MFMA per element type:
 //   fp32 : v_mfma_f32_16x16x4_f32   (4 per 16-byte fragment; lane group q holds k = 4q + e)
 //   bf16 : v_mfma_f32_16x16x32_bf16 (one per 16-byte fragment)
 //   fp8  : v_mfma_scale_f32_16x16x128_f8f6f4 with unit exponent scales, one per 128-byte stage, whose
@@ -168,9 +169,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
 {
     constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
     constexpr int ROWS = BM + NB;                      // LDS rows per stage (128 bytes each)
-    constexpr int CHUNKS = ROWS * 8;                   // 16-byte chunks per stage
     constexpr int NT = 64 * WAVES_M * WAVES_N;         // threads per block
-    constexpr int PER = (CHUNKS + NT - 1) / NT;        // chunks per thread
     constexpr int WM = BM / 16 / WAVES_M, WN = BN / 16 / WAVES_N;
     constexpr int KE = 128 / Elem<ET>::bytes;          // K elements per stage
     constexpr bool FP8 = ET == ET_FP8;
@@ -227,56 +226,125 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
     const float* W1s = FP8 ? (shared ? g.S1s : g.B1s + lgrp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
     const float* W3s = (FP8 && UP) ? (shared ? g.S3s : g.B3s + lgrp * (N / 128) * nkb) + ((n0 + wn0) / 128) * nkb : nullptr;
 
-    if (tid < BM) s_tok[tid] = tid < rows ? (UP ? g.row_token[row0 + tid] : row0 + tid) : -1;
-    __syncthreads();
-
-    // Per-thread source pointers of its chunks (fixed across K; advanced by 128 bytes per stage).
-    const uint8_t* src[PER];
-    int dst[PER];
-#pragma unroll
-    for (int p = 0; p < PER; p++) {
-        const int c = tid + p * NT;
-        src[p] = nullptr;
-        dst[p] = -1;
-        if (c < CHUNKS) {
-            const int row = c >> 3, ch = c & 7;
-            dst[p] = swz(row, ch);
-            if (row < BM) {
-                const int r = s_tok[row];
-                if (r >= 0) src[p] = g.A + (int64_t)r * g.lda + ch * 16;
-            } else if (row < BM + BN) {
-                src[p] = W1 + (int64_t)(n0 + row - BM) * ldb + ch * 16;
-            } else {
-                src[p] = W3 + (int64_t)(n0 + row - BM - BN) * ldb + ch * 16;
-            }
+    // A row of every tile row.  Rows past the tile's end: with fp8 operands they repeat the tile's first
+    // row (valid memory, finite values: computed, never stored); otherwise they are not loaded (-1).
+    if (tid < BM) {
+        if constexpr (FP8) {
+            const int r = tid < rows ? tid : 0;
+            s_tok[tid] = UP ? g.row_token[row0 + r] : row0 + r;
+        } else {
+            s_tok[tid] = tid < rows ? (UP ? g.row_token[row0 + tid] : row0 + tid) : -1;
         }
     }
-    i32x4 reg[PER];
+    __syncthreads();
+
     // K-stage order: rotated by the n-block, so blocks streaming weight rows at the same time read
     // different column offsets of them and spread over the HBM channels.  (The fp32 sum over K stages
     // then runs in a rotated but fixed order per output column: still deterministic.)
     const int nstages = K / KE;
     const int kshift = (nb * g.krot) % nstages;
     auto kst = [&](int s) { return s + kshift >= nstages ? s + kshift - nstages : s + kshift; };
-    auto load_stage = [&](int s0) {
-        const int s = kst(s0);
+
+    // Staging, bf16 and fp32: a 64-bit source pointer per 16-byte chunk (null for rows past the tile's
+    // end, which stay zero), advanced by 128 bytes per K stage.
+    constexpr int CHUNKS = ROWS * 8;                   // 16-byte chunks per stage
+    constexpr int PER = FP8 ? 1 : (CHUNKS + NT - 1) / NT;
+    const uint8_t* src[PER];
+    int dst[PER];
+    i32x4 reg[PER];
+    if constexpr (!FP8) {
 #pragma unroll
         for (int p = 0; p < PER; p++) {
-            reg[p] = (i32x4){0, 0, 0, 0};
-            if (src[p]) reg[p] = *(const i32x4*)(src[p] + (int64_t)s * 128);
+            const int c = tid + p * NT;
+            src[p] = nullptr;
+            dst[p] = -1;
+            if (c < CHUNKS) {
+                const int row = c >> 3, ch = c & 7;
+                dst[p] = swz(row, ch);
+                if (row < BM) {
+                    const int r = s_tok[row];
+                    if (r >= 0) src[p] = g.A + (int64_t)r * g.lda + ch * 16;
+                } else if (!UP || row < BM + BN) {
+                    src[p] = W1 + (int64_t)(n0 + row - BM) * ldb + ch * 16;
+                } else {
+                    src[p] = W3 + (int64_t)(n0 + row - BM - BN) * ldb + ch * 16;
+                }
+            }
+        }
+    }
+    // Staging, fp8: each region (A rows, W1 rows, W3 rows) is a block-uniform base plus a 32-bit per-lane
+    // offset fixed across K, and the K stage moves the base, so the loads take the scalar-base form with
+    // no per-load address arithmetic or branch: the fp8 kernels are bound by vector-ALU issue (the
+    // per-block rescaling of every MFMA result), and this frees it.  (The host keeps A and each expert's
+    // weights under 4 GB.)
+    constexpr int A_CH = BM * 8, B_CH = BN * 8;        // 16-byte chunks per stage: A tile, one B tile
+    constexpr int A_PER = FP8 ? (A_CH + NT - 1) / NT : 1, B_PER = FP8 ? (B_CH + NT - 1) / NT : 1;
+    constexpr bool A_EXACT = A_CH % NT == 0, B_EXACT = B_CH % NT == 0;
+    uint32_t offA[A_PER], offB[B_PER];
+    int dstA[A_PER], dstB[B_PER];
+    i32x4 ra[A_PER], rb1[B_PER], rb3[B_PER];
+    if constexpr (FP8) {
+#pragma unroll
+        for (int p = 0; p < A_PER; p++) {
+            const int c = A_EXACT ? tid + p * NT : min(tid + p * NT, A_CH - 1);
+            const int row = c >> 3, ch = c & 7;
+            offA[p] = (uint32_t)s_tok[row] * (uint32_t)g.lda + ch * 16;
+            dstA[p] = (A_EXACT || tid + p * NT < A_CH) ? swz(row, ch) : -1;
+        }
+#pragma unroll
+        for (int p = 0; p < B_PER; p++) {
+            const int c = B_EXACT ? tid + p * NT : min(tid + p * NT, B_CH - 1);
+            const int row = c >> 3, ch = c & 7;
+            offB[p] = (uint32_t)(n0 + row) * (uint32_t)ldb + ch * 16;
+            dstB[p] = (B_EXACT || tid + p * NT < B_CH) ? swz(BM + row, ch) : -1;
+        }
+    }
+
+    auto load_stage = [&](int s0) {
+        if constexpr (FP8) {
+            const int64_t koff = (int64_t)kst(s0) * 128;
+            const uint8_t* a = g.A + koff;
+            const uint8_t* b1 = W1 + koff;
+#pragma unroll
+            for (int p = 0; p < A_PER; p++) ra[p] = *(const i32x4*)(a + offA[p]);
+#pragma unroll
+            for (int p = 0; p < B_PER; p++) rb1[p] = *(const i32x4*)(b1 + offB[p]);
+            if constexpr (UP) {
+                const uint8_t* b3 = W3 + koff;
+#pragma unroll
+                for (int p = 0; p < B_PER; p++) rb3[p] = *(const i32x4*)(b3 + offB[p]);
+            }
+        } else {
+            const int s = kst(s0);
+#pragma unroll
+            for (int p = 0; p < PER; p++) {
+                reg[p] = (i32x4){0, 0, 0, 0};
+                if (src[p]) reg[p] = *(const i32x4*)(src[p] + (int64_t)s * 128);
+            }
         }
     };
     auto store_stage = [&](int buf) {
+        uint8_t* base = smem + buf * ROWS * 128;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int p = 0; p < PER; p++)
-            if (dst[p] >= 0) *(i32x4*)(smem + buf * ROWS * 128 + dst[p]) = reg[p];
+            for (int p = 0; p < A_PER; p++)
+                if (A_EXACT || dstA[p] >= 0) *(i32x4*)(base + dstA[p]) = ra[p];
+#pragma unroll
+            for (int p = 0; p < B_PER; p++) {
+                if (B_EXACT || dstB[p] >= 0) {
+                    *(i32x4*)(base + dstB[p]) = rb1[p];
+                    if constexpr (UP) *(i32x4*)(base + dstB[p] + BN * 128) = rb3[p];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < PER; p++)
+                if (dst[p] >= 0) *(i32x4*)(base + dst[p]) = reg[p];
+        }
     };
     auto load_scales = [&](int s, int buf) {
         if constexpr (FP8) {
-            if (tid < BM) {
-                const int r = s_tok[tid];
-                sA[buf][tid] = r >= 0 ? g.As[(int64_t)r * g.ldas + s] : 0.0f;
-            }
+            if (tid < BM) sA[buf][tid] = g.As[(int64_t)s_tok[tid] * g.ldas + s];
         }
     };
 

@@ -16,10 +16,11 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 int tile_rows(const moe_shape_t& s)
 {
     // By the average rows per routed expert: decode-sized groups -> 16-row tiles (weight streaming);
-    // ~100-200 rows -> 128-row tiles; larger groups -> 256-row tiles (more MFMA work per byte staged).
+    // otherwise 128-row tiles.  MOE_MAX_TILE_ROWS = 256 selects 256-row tiles for bf16 groups of more
+    // than 192 rows (measured no faster on MI355X, so off by default); fp8 and fp32 keep 128: the fp8
+    // per-K-block scaling accumulates in VGPRs, which caps the per-wave tile.
     const int64_t per_expert = s.T * s.k / (s.E > 0 ? s.E : 1);
     if (per_expert <= 24) return 16;
-    // fp8 keeps 128-row tiles: its per-K-block scaling accumulates in VGPRs, which caps the per-wave tile.
     if (per_expert <= 192 || s.act_dtype == MOE_F32 || s.w_dtype == MOE_FP8_E4M3) return 128;
     return MOE_MAX_TILE_ROWS;
 }
@@ -84,6 +85,13 @@ static moe_status_t check_shape(const moe_shape_t* s)
     if (!ok) return MOE_ERR_UNSUPPORTED;
     // int32 indexing of rows and elements inside the kernels
     if (s->T > (1 << 24) || (s->T * (s->k + 1)) * s->d > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+    // 32-bit byte offsets inside the GEMM operands: x, h, and one expert's weights each under 4 GB
+    const int64_t ab = s->act_dtype == MOE_F32 ? 4 : 2, wb = s->w_dtype == MOE_FP8_E4M3 ? 1 : ab;
+    const int64_t inter_max = s->inter > s->inter_shared ? s->inter : s->inter_shared;
+    const int64_t lim = (int64_t)1 << 32;
+    if (s->T * s->d * ab >= lim || s->T * (s->k + 1) * inter_max * ab >= lim ||
+        inter_max * s->d * wb >= lim)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
