@@ -437,6 +437,260 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
     }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Machinery of the direct-to-LDS forms below.  K stages are copied global -> LDS by the direct-to-LDS
+// load (global_load_lds_dwordx4: a wavefront's 64 lanes write 1 KB at M0 + 16 * lane), so staging uses
+// no registers, no LDS store instructions and no per-load vector-ALU work: each lane's source is a
+// block-uniform base in SGPRs (moved by the K stage) plus a 32-bit offset fixed for the whole K walk.
+// The loads are issued from asm, so the compiler knows of no load into LDS and schedules fragment reads
+// freely; an explicit vmcnt wait and barrier per stage order the reads after the loads of their stage.
+//
+// LDS row layout: 16-byte chunk c of row r stored at chunk c ^ f(r), f(r) = (r ^ (r >> 3 & 1)) & 7 for
+// 128-byte rows, ((r >> 1) ^ (r >> 3)) & 3 for 64-byte rows: a fragment read (lanes 0..31: 32
+// consecutive rows, one chunk) hits distinct banks for any 8 or 16 consecutive lanes, and f is unchanged
+// by adding 16 (resp. 32) rows.  The loads apply the swizzle on the source side (lane l writes stored
+// chunk l % (RB / 16) of row l / (RB / 16), so it reads the logical chunk that belongs there).
+// Rows past the tile's end load the tile's first row (valid memory); their results are never stored.
+// ---------------------------------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Barrier without the vmcnt(0) that __syncthreads implies: loads into the other ring buffers stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int RB> __device__ __forceinline__ int swzr(int row, int chunk)
+{
+    if constexpr (RB == 128) return row * 128 + ((chunk ^ ((row ^ (row >> 3 & 1)) & 7)) << 4);
+    else return row * 64 + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One direct-to-LDS load: lane l copies 16 bytes from sbase + voff to LDS address lds + 16 l.  M0 carries
+// the LDS address and is written here (one wait state before the load uses it); nothing else in the
+// kernels that use this keeps a value in M0.  No memory clobber: the load writes a ring buffer that no
+// LDS access nearby touches, and as a volatile asm it keeps its place relative to the barrier asm.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+// block -> (tile, n-block), the same mapping as grouped_gemm_kernel; false when the block has no work.
+__device__ __forceinline__ bool block_work(const GemmArgs& g, int& tile, int& nb)
+{
+    const int bid = blockIdx.x;
+    if (g.group_m == 0) {
+        tile = bid / g.n_blocks;
+        nb = bid % g.n_blocks;
+        return tile < *g.ntiles;
+    }
+    const int nt = *g.ntiles;
+    const int total = nt * g.n_blocks;
+    const int per = (total + 7) / 8;
+    if (bid >= 8 * per) return false;
+    const int l = (bid & 7) * per + (bid >> 3);
+    if (l >= total) return false;
+    const int items = g.group_m * g.n_blocks;
+    const int c = l / items, r = l % items;
+    const int gm = min(g.group_m, nt - c * g.group_m);
+    nb = r / gm;
+    tile = c * g.group_m + r % gm;
+    return true;
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Wide form for bf16 tiles of BM = 128 or 256 rows: each wavefront owns a 128 x 128 output block (UP:
+// 64 columns of W1 and the same 64 of W3) held in 16 accumulators of 32 x 32 (v_mfma_f32_32x32x16_bf16),
+// which needs the register file of one wavefront per SIMD.  Against a 64 x 128 block this cuts the LDS
+// bytes read per MFMA by a third.  Four wavefronts: BM = 128 -> 1 x 4 (block 128 x 512 output columns:
+// half the n-blocks of a 128 x 256 block, so x rows are fetched half as often), BM = 256 -> 2 x 2.
+// K stages of RB / 2 elements in a ring of NSTG, copied by direct-to-LDS loads; at the end of each stage
+// the barrier publishing the next stage, the refill of the freed buffer and the first fragment reads of
+// the next stage sit under the MFMAs of the stage's last K step.  With whole-line (128-byte) rows the
+// time of this kernel on MI355X is set by the global -> LDS copies (the same loop without MFMAs takes
+// 85-95 % of it), chiefly by the L2 misses of the weight panels and gathered x rows.
+// ---------------------------------------------------------------------------------------------------
+template <bool UP, int BM, int RB, int NSTG>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
+{
+    constexpr int WAVES_M = BM / 128, WAVES_N = 4 / WAVES_M;
+    constexpr int NJ = UP ? 2 : 4;                     // 32-column MFMA blocks per half (UP) or per wavefront
+    constexpr int WCOL = 32 * NJ;                      // wavefront columns (per half for UP)
+    constexpr int BN = WAVES_N * WCOL;                  // block columns (per half for UP)
+    constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
+    constexpr int ROWS = BM + NB;
+    constexpr int STAGE = ROWS * RB;
+    constexpr int CPR = RB / 16, RPL = 64 / CPR;       // 16-byte chunks per row, rows per 1-KB load
+    constexpr int PERW = ROWS / RPL / 4;               // 1-KB loads per wavefront per stage
+    constexpr int PA = BM / RPL / 4, PB1 = BN / RPL / 4; // ... of which A rows, W1 (or W2) rows
+    constexpr int KS = RB / 32;                        // 16-element K steps per stage
+    constexpr int NF = 4 + (UP ? 2 * NJ : NJ);         // fragment reads per K step
+    constexpr int NM = 4 * (UP ? 2 * NJ : NJ);         // MFMAs per K step
+    static_assert(BM == 128 || BM == 256, "128- or 256-row tiles");
+    static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
+    static_assert(ROWS % (4 * RPL) == 0 && (NSTG - 1) * PERW < 64, "loads per wavefront, vmcnt range");
+    static_assert(BM * 4 <= STAGE, "row table fits the first stage buffer");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STAGE];
+    int* s_tok = (int*)ring;                           // row table, dead before the first load into the ring
+
+    int tile, nb;
+    if (!block_work(g, tile, nb)) return;
+    const int4 td = g.tiles[tile];
+    const int grp = td.x, row0 = td.y, rows = td.z;
+    const bool shared = grp == g.E;
+    const int N = shared ? g.N_s : g.N_r, K = shared ? g.K_s : g.K_r;
+    const int n0 = nb * BN;
+    if (n0 >= N) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / WAVES_N) * 128, wn0 = (wave % WAVES_N) * WCOL;
+    const int64_t ldb = (shared ? g.ld_s : (int64_t)K) * 2;
+    const int64_t lgrp = grp - g.e_base;
+    const uint8_t* W1 = shared ? g.S1 : g.B1 + lgrp * N * ldb;
+    const uint8_t* W3 = UP ? (shared ? g.S3 : g.B3 + lgrp * N * ldb) : W1;
+
+    if (tid < BM) s_tok[tid] = UP ? g.row_token[row0 + (tid < rows ? tid : 0)] : row0 + (tid < rows ? tid : 0);
+    __syncthreads();
+    uint32_t off[PERW];
+#pragma unroll
+    for (int p = 0; p < PERW; p++) {
+        const int row = (4 * p + wave) * RPL + lane / CPR;
+        const int lc = (swzr<RB>(row, lane % CPR) - row * RB) >> 4;  // logical chunk stored at chunk lane % CPR
+        if (p < PA) off[p] = (uint32_t)s_tok[row] * (uint32_t)g.lda + lc * 16;
+        else if (p < PA + PB1) off[p] = (uint32_t)(n0 + row - BM) * (uint32_t)ldb + lc * 16;
+        else off[p] = (uint32_t)(n0 + row - BM - BN) * (uint32_t)ldb + lc * 16;
+    }
+    __syncthreads();                                   // the row table is dead from here
+
+    const int nstages = K / (RB / 2);
+    const uint32_t ring0 = lds_addr(ring);
+    auto issue = [&](int buf, int s) {
+        const int64_t koff = (int64_t)s * RB;
+        const uint8_t* a = g.A + koff;
+        const uint8_t* b1 = W1 + koff;
+        const uint8_t* b3 = W3 + koff;
+        const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
+#pragma unroll
+        for (int p = 0; p < PERW; p++) dma16(p < PA ? a : p < PA + PB1 ? b1 : b3, off[p], dst + p * 4096);
+    };
+
+    f32x16 acc1[4][NJ], acc3[4][UP ? NJ : 1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < NJ; j++) acc1[i][j] = (f32x16){};
+#pragma unroll
+        for (int j = 0; j < (UP ? NJ : 1); j++) acc3[i][j] = (f32x16){};
+    }
+
+    const int r32 = lane & 31, kh = lane >> 5;
+    struct Frags {
+        bf16x8 a[4], b1[NJ], b3[UP ? NJ : 1];
+    };
+    auto read = [&](int buf, int kk, Frags& f) {
+        const uint8_t* st = ring + buf * STAGE;
+        const int ch = 2 * kk + kh;
+#pragma unroll
+        for (int i = 0; i < 4; i++) f.a[i] = *(const bf16x8*)(st + swzr<RB>(wm0 + 32 * i + r32, ch));
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            f.b1[j] = *(const bf16x8*)(st + swzr<RB>(BM + wn0 + 32 * j + r32, ch));
+            if constexpr (UP) f.b3[j] = *(const bf16x8*)(st + swzr<RB>(BM + BN + wn0 + 32 * j + r32, ch));
+        }
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < NJ; j++) {
+                acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
+                if constexpr (UP) acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b3[j], acc3[i][j], 0, 0, 0);
+            }
+    };
+    // One K step: the fragments of the next step are read (one read after each of the first NF MFMAs).
+    auto kstep = [&](const Frags& cur, int buf_next, int kk_next, Frags& nxt) {
+        read(buf_next, kk_next, nxt);
+        mma(cur);
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // Ring: stage t lives in buffer t % NSTG.  The prologue loads stages 0 .. NSTG - 1; at the end of
+    // stage s (all its fragments read) stage s + 1 is awaited and published, and stage s's buffer is
+    // refilled with stage s + NSTG (past the end: the last stage again, into a buffer nobody reads), so
+    // NSTG - 1 stages are in flight while one is computed and every wait is the same vmcnt.
+#pragma unroll
+    for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1));
+    wait_vmcnt<(NSTG - 1) * PERW>();
+    lds_barrier();
+    Frags f0, f1;
+    read(0, 0, f0);
+    int buf = 0;
+    for (int s = 0; s + 1 < nstages; s++) {
+        const int nbuf = buf + 1 == NSTG ? 0 : buf + 1;
+        if constexpr (KS == 4) {
+            kstep(f0, buf, 1, f1);
+            kstep(f1, buf, 2, f0);
+            kstep(f0, buf, 3, f1);
+            wait_vmcnt<(NSTG - 2) * PERW>();
+            lds_barrier();
+            issue(buf, min(s + NSTG, nstages - 1));
+            kstep(f1, nbuf, 0, f0);
+        } else {
+            kstep(f0, buf, 1, f1);
+            wait_vmcnt<(NSTG - 2) * PERW>();
+            lds_barrier();
+            issue(buf, min(s + NSTG, nstages - 1));
+            kstep(f1, nbuf, 0, f0);
+        }
+        buf = nbuf;
+    }
+    if constexpr (KS == 4) {
+        kstep(f0, buf, 1, f1);
+        kstep(f1, buf, 2, f0);
+        kstep(f0, buf, 3, f1);
+        mma(f1);
+    } else {
+        kstep(f0, buf, 1, f1);
+        mma(f1);
+    }
+    wait_vmcnt<0>();                                   // no load may still target this block's LDS at exit
+
+    // Epilogue (32x32 accumulator layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4).
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int row = wm0 + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+            if (row >= rows) continue;
+            const int64_t orow = row0 + row;
+#pragma unroll
+            for (int j = 0; j < NJ; j++) {
+                const int col = n0 + wn0 + 32 * j + r32;
+                float v;
+                if constexpr (UP) v = silu_mul(round_bf16(acc1[i][j][r]), round_bf16(acc3[i][j][r]));
+                else v = acc1[i][j][r];
+                ((uint16_t*)g.out)[orow * g.ldo + col] = f32_to_bf16(v);
+            }
+        }
+}
+
 // fp8 activation quantisation of x: per row, per 128-column group, s = amax / 448 (1 if amax = 0),
 // codes = E4M3(round to nearest even)(x / s).  16 threads per group, 8 elements each.
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t ngroups, int d,
@@ -480,6 +734,33 @@ static void launch_one(GemmArgs a, hipStream_t stream)
     grouped_gemm_kernel<ET, UP, ACT_BF16, BM, BN, WAVES_M, WAVES_N, NBUF, MINW>
         <<<(unsigned)nblk, 64 * WAVES_M * WAVES_N, 0, stream>>>(a);
 }
+
+
+// Row bytes per K stage and ring depth of grouped_gemm_w_kernel (128-byte rows in a ring of two measured
+// best: 64-byte rows double the L2 requests, and deeper rings of them lose more than they hide).
+#ifndef MOE_W_RB
+#define MOE_W_RB 128
+#endif
+#ifndef MOE_W_NSTG
+#define MOE_W_NSTG 2
+#endif
+template <bool UP, int BM>
+static void launch_w(GemmArgs a, hipStream_t stream)
+{
+    const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
+    grouped_gemm_w_kernel<UP, BM, MOE_W_RB, MOE_W_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
+}
+
+// 1: bf16 up GEMMs with 128-row tiles use grouped_gemm_w_kernel when inter and the shared width are
+// multiples of 256, and 256-row tiles use it for both GEMMs.  MOE_LARGE_W_DN = 1 also sends the down
+// GEMM of 128-row tiles there when d is a multiple of 512 (measured slightly slower than
+// grouped_gemm_kernel on MI355X, so off by default).
+#ifndef MOE_LARGE_W
+#define MOE_LARGE_W 1
+#endif
+#ifndef MOE_LARGE_W_DN
+#define MOE_LARGE_W_DN 0
+#endif
 
 // Output features per block for the 128- and 256-row tile classes.
 #ifndef MOE_MID_UP_BN
@@ -616,9 +897,15 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
         if (bm == 16) {
             up.n_blocks = (int)(ws.inter_max / MOE_SMALL_UP_BN);
             launch_one<ET_BF16, true, true, 16, MOE_SMALL_UP_BN, 1, MOE_SMALL_UP_WAVES, 2, MOE_SMALL_UP_MINW>(up, stream);
+        } else if (bm == 128 && MOE_LARGE_W && s.inter % 256 == 0 && n_shared % 256 == 0) {
+            up.n_blocks = (int)(ws.inter_max / 256);
+            launch_w<true, 128>(up, stream);
         } else if (bm == 128) {
             up.n_blocks = (int)(ws.inter_max / MOE_MID_UP_BN);
             launch_one<ET_BF16, true, true, 128, MOE_MID_UP_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(up, stream);
+        } else if (MOE_LARGE_W) {
+            up.n_blocks = (int)(ws.inter_max / 128);
+            launch_w<true, 256>(up, stream);
         } else {
             up.n_blocks = (int)(ws.inter_max / 128);
             launch_one<ET_BF16, true, true, 256, 128, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(up, stream);
@@ -673,10 +960,16 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
         } else if (f32) {
             dn.n_blocks = (int)(s.d / 128);
             launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
+        } else if (MOE_LARGE_W && MOE_LARGE_W_DN && s.d % 512 == 0) {
+            dn.n_blocks = (int)(s.d / 512);
+            launch_w<false, 128>(dn, stream);
         } else {
             dn.n_blocks = (int)(s.d / MOE_MID_DN_BN);
             launch_one<ET_BF16, false, true, 128, MOE_MID_DN_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(dn, stream);
         }
+    } else if (MOE_LARGE_W) {
+        dn.n_blocks = (int)(s.d / 256);
+        launch_w<false, 256>(dn, stream);
     } else {
         dn.n_blocks = (int)(s.d / MOE_BIG_DN_BN);
         launch_one<ET_BF16, false, true, 256, MOE_BIG_DN_BN, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(dn, stream);
