@@ -453,6 +453,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
 // Rows past the tile's end load the tile's first row (valid memory); their results are never stored.
 // ---------------------------------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <int N> struct IntC {
+    static constexpr int value = N;
+};
 
 template <int N> __device__ __forceinline__ void wait_vmcnt()
 {
@@ -535,8 +538,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
     constexpr int PERW = ROWS / RPL / 4;               // 1-KB loads per wavefront per stage
     constexpr int PA = BM / RPL / 4, PB1 = BN / RPL / 4; // ... of which A rows, W1 (or W2) rows
     constexpr int KS = RB / 32;                        // 16-element K steps per stage
-    constexpr int NF = 4 + (UP ? 2 * NJ : NJ);         // fragment reads per K step
-    constexpr int NM = 4 * (UP ? 2 * NJ : NJ);         // MFMAs per K step
     static_assert(BM == 128 || BM == 256, "128- or 256-row tiles");
     static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
     static_assert(ROWS % (4 * RPL) == 0 && (NSTG - 1) * PERW < 64, "loads per wavefront, vmcnt range");
@@ -575,16 +576,29 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
     }
     __syncthreads();                                   // the row table is dead from here
 
+    // 32-row MFMA blocks holding tile rows: per wavefront (wave-uniform) and for the whole tile.  Blocks
+    // past the tile's end get no MFMAs and no fragment reads, and with a ring of two the A rows past the
+    // last computed block are not loaded either (with deeper rings every stage keeps the same number of
+    // loads per wavefront, which the vmcnt accounting below relies on).
+    const int nrb = max(0, min(4, (rows - wm0 + 31) / 32));
+    const int a_rows = NSTG == 2 ? min(BM, (rows + 31) / 32 * 32) : BM;
+
+    // K stages walked from a start rotated by the n-block (as in grouped_gemm_kernel), in a fixed order.
     const int nstages = K / (RB / 2);
+    const int kshift = (nb * g.krot) % nstages;
     const uint32_t ring0 = lds_addr(ring);
     auto issue = [&](int buf, int s) {
-        const int64_t koff = (int64_t)s * RB;
+        const int ks = s + kshift >= nstages ? s + kshift - nstages : s + kshift;
+        const int64_t koff = (int64_t)ks * RB;
         const uint8_t* a = g.A + koff;
         const uint8_t* b1 = W1 + koff;
         const uint8_t* b3 = W3 + koff;
         const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
 #pragma unroll
-        for (int p = 0; p < PERW; p++) dma16(p < PA ? a : p < PA + PB1 ? b1 : b3, off[p], dst + p * 4096);
+        for (int p = 0; p < PERW; p++) {
+            if (p < PA && (4 * p + wave) * RPL >= a_rows) continue;
+            dma16(p < PA ? a : p < PA + PB1 ? b1 : b3, off[p], dst + p * 4096);
+        }
     };
 
     f32x16 acc1[4][NJ], acc3[4][UP ? NJ : 1];
@@ -600,75 +614,94 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
     struct Frags {
         bf16x8 a[4], b1[NJ], b3[UP ? NJ : 1];
     };
-    auto read = [&](int buf, int kk, Frags& f) {
-        const uint8_t* st = ring + buf * STAGE;
-        const int ch = 2 * kk + kh;
-#pragma unroll
-        for (int i = 0; i < 4; i++) f.a[i] = *(const bf16x8*)(st + swzr<RB>(wm0 + 32 * i + r32, ch));
-#pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            f.b1[j] = *(const bf16x8*)(st + swzr<RB>(BM + wn0 + 32 * j + r32, ch));
-            if constexpr (UP) f.b3[j] = *(const bf16x8*)(st + swzr<RB>(BM + BN + wn0 + 32 * j + r32, ch));
-        }
-    };
-    auto mma = [&](const Frags& f) {
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < NJ; j++) {
-                acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
-                if constexpr (UP) acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b3[j], acc3[i][j], 0, 0, 0);
-            }
-    };
-    // One K step: the fragments of the next step are read (one read after each of the first NF MFMAs).
-    auto kstep = [&](const Frags& cur, int buf_next, int kk_next, Frags& nxt) {
-        read(buf_next, kk_next, nxt);
-        mma(cur);
-#pragma unroll
-        for (int m = 0; m < NM; m++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-    };
 
-    // Ring: stage t lives in buffer t % NSTG.  The prologue loads stages 0 .. NSTG - 1; at the end of
-    // stage s (all its fragments read) stage s + 1 is awaited and published, and stage s's buffer is
-    // refilled with stage s + NSTG (past the end: the last stage again, into a buffer nobody reads), so
-    // NSTG - 1 stages are in flight while one is computed and every wait is the same vmcnt.
+    // The K loop for NRB computed row blocks (a compile-time count, so the MFMA / fragment-read
+    // interleave below stays one straight-line schedule).
+    auto k_loop = [&](auto nrb_tag) {
+        constexpr int NRB = decltype(nrb_tag)::value;
+        constexpr int NF = NRB == 0 ? 0 : NRB + (UP ? 2 * NJ : NJ);   // fragment reads per K step
+        constexpr int NM = NRB * (UP ? 2 * NJ : NJ);                   // MFMAs per K step
+        auto read = [&](int buf, int kk, Frags& f) {
+            if constexpr (NRB > 0) {
+                const uint8_t* st = ring + buf * STAGE;
+                const int ch = 2 * kk + kh;
 #pragma unroll
-    for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1));
-    wait_vmcnt<(NSTG - 1) * PERW>();
-    lds_barrier();
-    Frags f0, f1;
-    read(0, 0, f0);
-    int buf = 0;
-    for (int s = 0; s + 1 < nstages; s++) {
-        const int nbuf = buf + 1 == NSTG ? 0 : buf + 1;
+                for (int i = 0; i < NRB; i++) f.a[i] = *(const bf16x8*)(st + swzr<RB>(wm0 + 32 * i + r32, ch));
+#pragma unroll
+                for (int j = 0; j < NJ; j++) {
+                    f.b1[j] = *(const bf16x8*)(st + swzr<RB>(BM + wn0 + 32 * j + r32, ch));
+                    if constexpr (UP) f.b3[j] = *(const bf16x8*)(st + swzr<RB>(BM + BN + wn0 + 32 * j + r32, ch));
+                }
+            }
+        };
+        auto mma = [&](const Frags& f) {
+#pragma unroll
+            for (int i = 0; i < NRB; i++)
+#pragma unroll
+                for (int j = 0; j < NJ; j++) {
+                    acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
+                    if constexpr (UP)
+                        acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b3[j], acc3[i][j], 0, 0, 0);
+                }
+        };
+        // One K step: the fragments of the next step are read (one read after each of the first NF MFMAs).
+        auto kstep = [&](const Frags& cur, int buf_next, int kk_next, Frags& nxt) {
+            read(buf_next, kk_next, nxt);
+            mma(cur);
+#pragma unroll
+            for (int m = 0; m < NM; m++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (m < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        };
+
+        // Ring: stage t lives in buffer t % NSTG.  The prologue loads stages 0 .. NSTG - 1; at the end of
+        // stage s (all its fragments read) stage s + 1 is awaited and published, and stage s's buffer is
+        // refilled with stage s + NSTG (past the end: the last stage again, into a buffer nobody reads), so
+        // NSTG - 1 stages are in flight while one is computed and every wait is the same vmcnt.
+#pragma unroll
+        for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1));
+        // (a ring of two may skip A loads, so its stages can hold fewer than PERW loads: wait for both)
+        wait_vmcnt<NSTG == 2 ? 0 : (NSTG - 1) * PERW>();
+        lds_barrier();
+        Frags f0, f1;
+        read(0, 0, f0);
+        int buf = 0;
+        for (int s = 0; s + 1 < nstages; s++) {
+            const int nbuf = buf + 1 == NSTG ? 0 : buf + 1;
+            if constexpr (KS == 4) {
+                kstep(f0, buf, 1, f1);
+                kstep(f1, buf, 2, f0);
+                kstep(f0, buf, 3, f1);
+                wait_vmcnt<(NSTG - 2) * PERW>();
+                lds_barrier();
+                issue(buf, min(s + NSTG, nstages - 1));
+                kstep(f1, nbuf, 0, f0);
+            } else {
+                kstep(f0, buf, 1, f1);
+                wait_vmcnt<(NSTG - 2) * PERW>();
+                lds_barrier();
+                issue(buf, min(s + NSTG, nstages - 1));
+                kstep(f1, nbuf, 0, f0);
+            }
+            buf = nbuf;
+        }
         if constexpr (KS == 4) {
             kstep(f0, buf, 1, f1);
             kstep(f1, buf, 2, f0);
             kstep(f0, buf, 3, f1);
-            wait_vmcnt<(NSTG - 2) * PERW>();
-            lds_barrier();
-            issue(buf, min(s + NSTG, nstages - 1));
-            kstep(f1, nbuf, 0, f0);
+            mma(f1);
         } else {
             kstep(f0, buf, 1, f1);
-            wait_vmcnt<(NSTG - 2) * PERW>();
-            lds_barrier();
-            issue(buf, min(s + NSTG, nstages - 1));
-            kstep(f1, nbuf, 0, f0);
+            mma(f1);
         }
-        buf = nbuf;
-    }
-    if constexpr (KS == 4) {
-        kstep(f0, buf, 1, f1);
-        kstep(f1, buf, 2, f0);
-        kstep(f0, buf, 3, f1);
-        mma(f1);
-    } else {
-        kstep(f0, buf, 1, f1);
-        mma(f1);
+    };
+    switch (nrb) {
+    case 4: k_loop(IntC<4>{}); break;
+    case 3: k_loop(IntC<3>{}); break;
+    case 2: k_loop(IntC<2>{}); break;
+    case 1: k_loop(IntC<1>{}); break;
+    default: k_loop(IntC<0>{}); break;
     }
     wait_vmcnt<0>();                                   // no load may still target this block's LDS at exit
 
@@ -744,11 +777,24 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 #ifndef MOE_W_NSTG
 #define MOE_W_NSTG 2
 #endif
+#ifndef MOE_W256_RB
+#define MOE_W256_RB 128
+#endif
+#ifndef MOE_W256_NSTG
+#define MOE_W256_NSTG 2
+#endif
+#ifndef MOE_KROT_W
+#define MOE_KROT_W 3
+#endif
 template <bool UP, int BM>
 static void launch_w(GemmArgs a, hipStream_t stream)
 {
+    a.krot = MOE_KROT_W;
     const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
-    grouped_gemm_w_kernel<UP, BM, MOE_W_RB, MOE_W_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
+    if constexpr (BM == 128)
+        grouped_gemm_w_kernel<UP, BM, MOE_W_RB, MOE_W_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
+    else
+        grouped_gemm_w_kernel<UP, BM, MOE_W256_RB, MOE_W256_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
 }
 
 // 1: bf16 up GEMMs with 128-row tiles use grouped_gemm_w_kernel when inter and the shared width are
@@ -777,6 +823,9 @@ static void launch_w(GemmArgs a, hipStream_t stream)
 #endif
 #ifndef MOE_GROUP_M
 #define MOE_GROUP_M 8
+#endif
+#ifndef MOE_GROUP_M_256
+#define MOE_GROUP_M_256 8
 #endif
 #ifndef MOE_FP8_WM
 #define MOE_FP8_WM 2
@@ -849,7 +898,7 @@ static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws, int e_base)
     a.ntiles = ws.sync;
     a.max_tiles = (int)ws.max_tiles;
     a.E = (int)s.E;
-    a.group_m = tile_rows(s) > 16 ? MOE_GROUP_M : 0;
+    a.group_m = tile_rows(s) == 16 ? 0 : tile_rows(s) == 256 ? MOE_GROUP_M_256 : MOE_GROUP_M;
     return a;
 }
 

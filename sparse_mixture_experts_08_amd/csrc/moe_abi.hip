@@ -8,20 +8,24 @@
 namespace moe {
 
 #ifndef MOE_MAX_TILE_ROWS
-#define MOE_MAX_TILE_ROWS 128
+#define MOE_MAX_TILE_ROWS 256
+#endif
+#ifndef MOE_T256_MIN
+#define MOE_T256_MIN 24
 #endif
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int tile_rows(const moe_shape_t& s)
 {
-    // By the average rows per routed expert: decode-sized groups -> 16-row tiles (weight streaming);
-    // otherwise 128-row tiles.  MOE_MAX_TILE_ROWS = 256 selects 256-row tiles for bf16 groups of more
-    // than 192 rows (measured no faster on MI355X, so off by default); fp8 and fp32 keep 128: the fp8
-    // per-K-block scaling accumulates in VGPRs, which caps the per-wave tile.
+    // By the average rows per routed expert: decode-sized groups (<= 24 rows) -> 16-row tiles (weight
+    // streaming).  Otherwise bf16 takes 256-row tiles: an expert of up to 256 rows reads its weights once,
+    // and a 256 x 256 output block needs fewer staged bytes per MFMA than 128 x 512; row blocks past a
+    // tile's end are skipped.  fp8 and fp32 keep 128: the fp8 per-K-block scaling accumulates in VGPRs,
+    // which caps the per-wave tile.
     const int64_t per_expert = s.T * s.k / (s.E > 0 ? s.E : 1);
     if (per_expert <= 24) return 16;
-    if (per_expert <= 192 || s.act_dtype == MOE_F32 || s.w_dtype == MOE_FP8_E4M3) return 128;
+    if (per_expert <= MOE_T256_MIN || s.act_dtype == MOE_F32 || s.w_dtype == MOE_FP8_E4M3) return 128;
     return MOE_MAX_TILE_ROWS;
 }
 
