@@ -161,6 +161,74 @@ __device__ __forceinline__ void mma_stage(const uint8_t* As_lds, const uint8_t* 
     }
 }
 
+// Epilogue of the 16x16-MFMA kernels.  Accumulator layout: lane holds rows 4*(lane/16) + r, column
+// lane % 16.  UP: h = round(silu(round g) * round u), with fp8 weights quantised per 1x128 group through
+// `smem` (BM x BN floats; the caller has finished with the staging buffers); down: y rows = round(acc).
+template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WM, int WN, int NT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, uint8_t* smem, const f32x4 (&acc1)[WM][WN],
+                                              const f32x4 (&acc3)[WM][WN], int rows, int row0, int n0, int wm0,
+                                              int wn0, int tid)
+{
+    constexpr bool FP8 = ET == ET_FP8;
+    const int lane = tid & 63;
+    const int r16 = lane & 15, q = lane >> 4;
+    if constexpr (UP && FP8) {
+        float* hs = (float*)smem;                      // [BM][BN] h values, then quantised per 128 group
+#pragma unroll
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int j = 0; j < WN; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float gg = round_bf16(acc1[i][j][r]), uu = round_bf16(acc3[i][j][r]);
+                    hs[(wm0 + i * 16 + 4 * q + r) * BN + wn0 + j * 16 + r16] = round_bf16(silu_mul(gg, uu));
+                }
+        __syncthreads();
+        // 16 threads per (row, 128-column group), 8 columns each
+        constexpr int GROUPS = BM * (BN / 128);
+        for (int gi = tid >> 4; gi < GROUPS; gi += NT / 16) {
+            const int row = gi / (BN / 128), grp128 = gi % (BN / 128);
+            const int sub = tid & 15;
+            const float* v = hs + row * BN + grp128 * 128 + sub * 8;
+            float amax = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+            if (row < rows) {
+                uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
+                uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+                const int64_t orow = row0 + row;
+                *(uint2*)(g.out + orow * g.ldo + n0 + grp128 * 128 + sub * 8) = make_uint2(lo, hi);
+                if (sub == 0) g.outs[orow * g.ldos + (n0 + grp128 * 128) / 128] = sc;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = wm0 + i * 16 + 4 * q + r;
+                if (row >= rows) continue;
+                const int64_t orow = row0 + row;
+#pragma unroll
+                for (int j = 0; j < WN; j++) {
+                    const int col = n0 + wn0 + j * 16 + r16;
+                    float v;
+                    if constexpr (UP) {
+                        const float gg = round_act<ACT_BF16>(acc1[i][j][r]), uu = round_act<ACT_BF16>(acc3[i][j][r]);
+                        v = silu_mul(gg, uu);
+                    } else {
+                        v = acc1[i][j][r];
+                    }
+                    if constexpr (ACT_BF16) ((uint16_t*)g.out)[orow * g.ldo + col] = f32_to_bf16(v);
+                    else ((float*)g.out)[orow * g.ldo + col] = v;
+                }
+            }
+    }
+}
+
 // NBUF: LDS stages (2 = double buffered, one barrier per K stage; 1 = single buffer, two barriers per
 // stage but half the LDS, so two blocks share a CU and cover each other's barriers).  MINW: minimum
 // wavefronts per SIMD the register allocation must allow.
@@ -376,65 +444,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
         __syncthreads();
     }
 
-    // ---------------------------------------------------------------------------------------------
-    // Epilogue.  Accumulator layout (16x16 MFMA): lane holds rows 4*(lane/16) + r, column lane % 16.
-    // ---------------------------------------------------------------------------------------------
-    const int r16 = lane & 15, q = lane >> 4;
-    if constexpr (UP && FP8) {
-        float* hs = (float*)smem;                      // [BM][BN] h values, then quantised per 128 group
-#pragma unroll
-        for (int i = 0; i < WM; i++)
-#pragma unroll
-            for (int j = 0; j < WN; j++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float gg = round_bf16(acc1[i][j][r]), uu = round_bf16(acc3[i][j][r]);
-                    hs[(wm0 + i * 16 + 4 * q + r) * BN + wn0 + j * 16 + r16] = round_bf16(silu_mul(gg, uu));
-                }
-        __syncthreads();
-        // 16 threads per (row, 128-column group), 8 columns each
-        constexpr int GROUPS = BM * (BN / 128);
-        for (int gi = tid >> 4; gi < GROUPS; gi += NT / 16) {
-            const int row = gi / (BN / 128), grp128 = gi % (BN / 128);
-            const int sub = tid & 15;
-            const float* v = hs + row * BN + grp128 * 128 + sub * 8;
-            float amax = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-            if (row < rows) {
-                uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
-                uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
-                const int64_t orow = row0 + row;
-                *(uint2*)(g.out + orow * g.ldo + n0 + grp128 * 128 + sub * 8) = make_uint2(lo, hi);
-                if (sub == 0) g.outs[orow * g.ldos + (n0 + grp128 * 128) / 128] = sc;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < WM; i++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int row = wm0 + i * 16 + 4 * q + r;
-                if (row >= rows) continue;
-                const int64_t orow = row0 + row;
-#pragma unroll
-                for (int j = 0; j < WN; j++) {
-                    const int col = n0 + wn0 + j * 16 + r16;
-                    float v;
-                    if constexpr (UP) {
-                        const float gg = round_act<ACT_BF16>(acc1[i][j][r]), uu = round_act<ACT_BF16>(acc3[i][j][r]);
-                        v = silu_mul(gg, uu);
-                    } else {
-                        v = acc1[i][j][r];
-                    }
-                    if constexpr (ACT_BF16) ((uint16_t*)g.out)[orow * g.ldo + col] = f32_to_bf16(v);
-                    else ((float*)g.out)[orow * g.ldo + col] = v;
-                }
-            }
-    }
+    gemm_epilogue<ET, UP, ACT_BF16, BM, BN, WM, WN, NT>(g, smem, acc1, acc3, rows, row0, n0, wm0, wn0, tid);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -485,6 +495,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "m0");
+}
+// The 4-byte form: lane l copies 4 bytes from sbase + voff to LDS address lds + 4 l.
+__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "m0");
 }
 #pragma clang diagnostic pop
@@ -724,6 +740,123 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
         }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// fp8 form with direct-to-LDS staging (128-row tiles, eight wavefronts as 2 x 4, the 16x16x128 fp8 MFMA
+// and per-K-block rescaling of mma_stage).  A K stage is 128 fp8 elements: one 128-byte line of every A
+// row, W1 row and W3 row, stored as in grouped_gemm_kernel (16-byte chunks XOR-swizzled by row), so
+// mma_stage reads it unchanged.  The stages sit in a ring of NSTG buffers filled by global_load_lds (no
+// staging registers, no LDS stores), NSTG - 1 of them in flight while one is computed.  The scales of a
+// stage ride in the same ring: wavefronts 0-1 copy the A row scales of the stage (one 4-byte load per
+// row), wavefront 2 the W1 block scales, wavefront 3 the W3 block scales, the others a dummy copy, so
+// every wavefront issues the same number of loads per stage and one vmcnt value waits for a stage.
+// ---------------------------------------------------------------------------------------------------
+template <bool UP, int BN, int NSTG>
+__global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
+{
+    constexpr int BM = 128, WAVES_M = 2, WAVES_N = 4, NW = 8, NT = 512;
+    constexpr int WM = BM / 16 / WAVES_M, WN = BN / 16 / WAVES_N;
+    constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
+    constexpr int ROWS = BM + NB;                      // 128-byte LDS rows per stage
+    constexpr int STAGE = ROWS * 128;
+    constexpr int LOADS = ROWS / 8;                    // 1-KB loads per stage
+    constexpr int PERW = LOADS / NW;                   // ... per wavefront
+    constexpr int PA = BM / 8 / NW;                    // ... of which A rows
+    constexpr int PB1 = BN / 8 / NW;                   // ... W1 (or W2) rows
+    constexpr int NL = PERW + 1;                       // loads per wavefront per stage (with the scale copy)
+    static_assert(LOADS % NW == 0 && BN % 128 == 0 && BN / 128 <= 64, "whole loads per wavefront");
+    static_assert(WN * 16 <= 128 && 128 % (WN * 16) == 0, "a wavefront's columns share one fp8 block scale");
+    static_assert((NSTG - 1) * NL < 64, "vmcnt range");
+    static_assert(!UP || BM * BN * 4 <= NSTG * STAGE, "h tile must fit the ring");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STAGE];
+    __shared__ __attribute__((aligned(256))) float scl[NSTG][NW * 64];   // per stage: A row scales, W1, W3 block scales
+    __shared__ int s_tok[BM];
+
+    int tile, nb;
+    if (!block_work(g, tile, nb)) return;
+    const int4 td = g.tiles[tile];
+    const int grp = td.x, row0 = td.y, rows = td.z;
+    const bool shared = grp == g.E;
+    const int N = shared ? g.N_s : g.N_r, K = shared ? g.K_s : g.K_r;
+    const int n0 = nb * BN;
+    if (n0 >= N) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / WAVES_N) * WM * 16, wn0 = (wave % WAVES_N) * WN * 16;
+    const int64_t ldb = shared ? g.ld_s : (int64_t)K;  // bytes per weight row
+    const int64_t lgrp = grp - g.e_base;
+    const uint8_t* W1 = shared ? g.S1 : g.B1 + lgrp * N * ldb;
+    const uint8_t* W3 = UP ? (shared ? g.S3 : g.B3 + lgrp * N * ldb) : W1;
+    const int nkb = shared ? g.nkb_s : K / 128;        // scale blocks per weight-scale row
+    const float* W1s = (shared ? g.S1s : g.B1s + lgrp * (N / 128) * nkb) + (n0 / 128) * nkb;
+    const float* W3s = UP ? (shared ? g.S3s : g.B3s + lgrp * (N / 128) * nkb) + (n0 / 128) * nkb : W1s;
+
+    // rows past the tile's end repeat its first row (valid memory, finite values; never stored)
+    if (tid < BM) s_tok[tid] = UP ? g.row_token[row0 + (tid < rows ? tid : 0)] : row0 + (tid < rows ? tid : 0);
+    __syncthreads();
+
+    // Per-lane source offsets, fixed over the K walk.  Load p of wavefront w fills LDS rows
+    // (p * NW + w) * 8 .. + 8; lane l writes stored chunk l % 8 of row l / 8, which holds the logical chunk
+    // (l % 8) ^ (row % 8).
+    uint32_t off[PERW];
+#pragma unroll
+    for (int p = 0; p < PERW; p++) {
+        const int row = (p * NW + wave) * 8 + (lane >> 3);
+        const int lc = (lane & 7) ^ (row & 7);
+        if (p < PA) off[p] = (uint32_t)s_tok[row] * (uint32_t)g.lda + lc * 16;
+        else if (p < PA + PB1) off[p] = (uint32_t)(n0 + row - BM) * (uint32_t)ldb + lc * 16;
+        else off[p] = (uint32_t)(n0 + row - BM - BN) * (uint32_t)ldb + lc * 16;
+    }
+    // scale copy of this wavefront: byte offset from its base, the base moved by the K stage below
+    uint32_t soff = 0;
+    if (wave < 2) soff = (uint32_t)s_tok[wave * 64 + lane] * (uint32_t)g.ldas * 4u;
+    else if (wave == 2 || (UP && wave == 3)) soff = (uint32_t)(lane < BN / 128 ? lane : 0) * (uint32_t)nkb * 4u;
+
+    const int nstages = K / 128;
+    const int kshift = (nb * g.krot) % nstages;
+    const uint32_t ring0 = lds_addr(ring), scl0 = lds_addr(&scl[0][0]);
+    auto issue = [&](int buf, int s) {
+        const int ks = s + kshift >= nstages ? s + kshift - nstages : s + kshift;
+        const int64_t koff = (int64_t)ks * 128;
+        const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
+#pragma unroll
+        for (int p = 0; p < PERW; p++) dma16((p < PA ? g.A : p < PA + PB1 ? W1 : W3) + koff, off[p], dst + p * NW * 1024);
+        const uint8_t* sb = wave < 2 ? (const uint8_t*)(g.As + ks)
+                          : wave == 2 ? (const uint8_t*)(W1s + ks)
+                          : (UP && wave == 3) ? (const uint8_t*)(W3s + ks) : (const uint8_t*)W1s;
+        dma4(sb, soff, scl0 + (buf * NW * 64 + wave * 64) * 4);
+    };
+
+    f32x4 acc1[WM][WN], acc3[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < WN; j++) acc1[i][j] = acc3[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int cb = wn0 / 128;                          // the wavefront's weight block within the n-block
+#pragma unroll
+    for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1));
+    wait_vmcnt<(NSTG - 1) * NL>();
+    lds_barrier();
+    int buf = 0;
+    for (int s = 0; s < nstages; s++) {
+        const float* sc = scl[buf];
+        const uint8_t* st = ring + buf * STAGE;
+        mma_stage<ET_FP8, UP, WM, WN, BN>(st, st + BM * 128, sc, sc[128 + cb], UP ? sc[192 + cb] : 0.f, wm0, wn0,
+                                         lane, acc1, acc3);
+        if (s + 1 < nstages) {
+            wait_vmcnt<(NSTG - 2) * NL>();             // stage s + 1 has landed
+            lds_barrier();                             // ... for every wavefront; stage s is read
+            issue(buf, min(s + NSTG, nstages - 1));    // past the end: the last stage again (never read)
+            buf = buf + 1 == NSTG ? 0 : buf + 1;
+        }
+    }
+    wait_vmcnt<0>();                                   // no load may still target this block's LDS
+    lds_barrier();
+    gemm_epilogue<ET_FP8, UP, true, BM, BN, WM, WN, NT>(g, ring, acc1, acc3, rows, row0, n0, wm0, wn0, tid);
+}
+
 // fp8 activation quantisation of x: per row, per 128-column group, s = amax / 448 (1 if amax = 0),
 // codes = E4M3(round to nearest even)(x / s).  16 threads per group, 8 elements each.
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t ngroups, int d,
@@ -795,6 +928,20 @@ static void launch_w(GemmArgs a, hipStream_t stream)
         grouped_gemm_w_kernel<UP, BM, MOE_W_RB, MOE_W_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
     else
         grouped_gemm_w_kernel<UP, BM, MOE_W256_RB, MOE_W256_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
+}
+
+#ifndef MOE_F8_NSTG
+#define MOE_F8_NSTG 3
+#endif
+// 1: fp8 GEMMs with 128-row tiles use grouped_gemm_f8_kernel (direct-to-LDS staging).
+#ifndef MOE_F8_DMA
+#define MOE_F8_DMA 1
+#endif
+template <bool UP, int BN>
+static void launch_f8(GemmArgs a, hipStream_t stream)
+{
+    const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
+    grouped_gemm_f8_kernel<UP, BN, MOE_F8_NSTG><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
 
 // 1: bf16 up GEMMs with 128-row tiles use grouped_gemm_w_kernel when inter and the shared width are
@@ -937,6 +1084,7 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     if (fp8) {
         up.n_blocks = (int)(ws.inter_max / 128);
         if (bm == 16) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
+        else if (MOE_F8_DMA) launch_f8<true, 128>(up, stream);
         else launch_one<ET_FP8, true, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(up, stream);
     } else if (f32) {
         up.n_blocks = (int)(ws.inter_max / 64);
@@ -998,14 +1146,16 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     } else if (s.d % 256) {
         // d an odd multiple of 128: 128-wide n-blocks (the wider configurations need d % 256 == 0)
         dn.n_blocks = (int)(s.d / 128);
-        if (fp8) launch_one<ET_FP8, false, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
+        if (fp8 && MOE_F8_DMA) launch_f8<false, 128>(dn, stream);
+        else if (fp8) launch_one<ET_FP8, false, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
         else if (f32) launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
         else if (bm == 128) launch_one<ET_BF16, false, true, 128, 128, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(dn, stream);
         else launch_one<ET_BF16, false, true, 256, 128, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(dn, stream);
     } else if (bm == 128) {
         if (fp8) {
             dn.n_blocks = (int)(s.d / MOE_FP8_DN_BN);
-            launch_one<ET_FP8, false, true, 128, MOE_FP8_DN_BN, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
+            if (MOE_F8_DMA) launch_f8<false, MOE_FP8_DN_BN>(dn, stream);
+            else launch_one<ET_FP8, false, true, 128, MOE_FP8_DN_BN, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
         } else if (f32) {
             dn.n_blocks = (int)(s.d / 128);
             launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
