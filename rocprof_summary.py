@@ -1,0 +1,118 @@
+"""Summarise the rocprofv3 runs of one bench.py workload into profiles/.
+
+python rocprof_summary.py WORKLOAD VARIANT TRACE_DIR FETCH_DIR WRITE_DIR
+
+TRACE_DIR holds the CSV output of `rocprofv3 --kernel-trace --stats -f csv -o run`, FETCH_DIR and WRITE_DIR
+that of `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` over a bench.py run that ends with one plain
+1 GiB device copy (`--copy-calibration-mib 1024`).  Writes profiles/kernels_<workload>[_<variant>].md
+(kernel durations and HBM bytes per dispatch) and records the grouped GEMMs' bytes per launch, scaled by
+what the counters read for the known-size copy, in profiles/traffic.json under the hash of the GEMM
+source they were taken on (bench.py reports them only while that hash matches).
+"""
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_08_amd", "csrc", "gemm.hip")
+COPY_KIB = 1 << 20  # the calibration copy: 1 GiB read and 1 GiB written
+
+
+def _csv(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return [r for f in files for r in csv.DictReader(open(f))]
+
+
+def _counter(d, name):
+    """Average value of counter `name` per dispatch, by kernel name; the copy kernel's entry is its largest
+    dispatch (the 1 GiB calibration copy; the run's other copies are small input transfers)."""
+    vals = defaultdict(list)
+    for r in _csv(d, "counter_collection.csv"):
+        if r["Counter_Name"] == name:
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: ((max(v), 1) if "copyBuffer" in k else (sum(v) / len(v), len(v))) for k, v in vals.items()}
+
+
+def gemm_role(kernel):
+    """'up_gemm' / 'down_gemm' for the grouped GEMM kernels, else None."""
+    m = re.search(r"grouped_gemm_(w_|f8_)?kernel<([^>]*)>", kernel)
+    if not m:
+        return None
+    args = [a.strip() for a in m.group(2).split(",")]
+    up = args[1] if m.group(1) is None else args[0]
+    return "up_gemm" if up == "true" else "down_gemm"
+
+
+def main():
+    workload, variant, trace_dir, fetch_dir, write_dir = sys.argv[1:6]
+    key = workload if variant == "layer" else f"{workload}/{variant}"
+    stats = _csv(trace_dir, "kernel_stats.csv")
+    fetch, write = _counter(fetch_dir, "FETCH_SIZE"), _counter(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy or not [k for k in write if "copyBuffer" in k]:
+        raise SystemExit("no calibration copy in the counter runs")
+    ff = COPY_KIB / fetch[copy[0]][0]
+    wf = COPY_KIB / write[[k for k in write if "copyBuffer" in k][0]][0]
+
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    moe = [r for r in stats if "moe::" in r["Name"]]
+    lines = [f"# rocprofv3 kernel summary: {key}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; R = repository root):", "", "```"]
+    v = f" --variant {variant}"
+    bench = f"python3 $R/bench.py --workload {workload}{v}"
+    lines.append(f"rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o run -- {bench} "
+                 "--steps 10 --warmup 2 --no-cpu-baseline")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f'rocprofv3 --pmc {c} --kernel-include-regex "moe::|copyBuffer" -f csv -d '
+                     f"$R/gpurun_out/prof_{c} -o run -- {bench} --steps 1 --warmup 1 --no-cpu-baseline "
+                     "--copy-calibration-mib 1024")
+    lines.append(f"python3 $R/rocprof_summary.py {workload} {variant} $R/gpurun_out/prof_trace "
+                 "$R/gpurun_out/prof_FETCH_SIZE $R/gpurun_out/prof_WRITE_SIZE")
+    lines += ["```", "", "## Kernel durations (--kernel-trace --stats; every dispatch in the run, including the "
+              "staged pass)", "", "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in moe:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", "## HBM traffic per dispatch (--pmc, averaged over dispatches)", "",
+              f"Calibration: one plain device copy of 1 GiB (torch copy_, dispatched as `{copy[0]}`) reads "
+              f"FETCH_SIZE = {fetch[copy[0]][0]:.0f} KiB and WRITE_SIZE = "
+              f"{write[[k for k in write if 'copyBuffer' in k][0]][0]:.0f} KiB; scale factors FETCH x{ff:.3f}, "
+              f"WRITE x{wf:.3f}.", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB (scaled) | written GB (scaled) |",
+              "|---|---|---|---|---|---|"]
+    rec = {"gemm_source_sha256_16": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16],
+           "fetch_factor": ff, "write_factor": wf}
+    for k in sorted(fetch):
+        if "moe::" not in k:
+            continue
+        fk, n = fetch[k]
+        wk = write.get(k, (0.0, 0))[0]
+        rb, wb = fk * 1024 * ff / 1e9, wk * 1024 * wf / 1e9
+        lines.append(f"| `{k}` | {n} | {fk:.0f} | {wk:.0f} | {rb:.3f} | {wb:.4f} |")
+        role = gemm_role(k)
+        if role:
+            rec[role] = {"kernel": k, "bytes": (rb + wb) * 1e9}
+    lines += ["", f"Kernel source hash (sha256[:16] of csrc/gemm.hip) when measured: `{rec['gemm_source_sha256_16']}`",
+              ""]
+    name = f"kernels_{workload}" + ("" if variant == "layer" else f"_{variant}") + ".md"
+    open(os.path.join(ROOT, "profiles", name), "w").write("\n".join(lines))
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        traffic = json.load(open(tpath))
+    except (OSError, ValueError):
+        traffic = {}
+    traffic[key] = rec
+    json.dump(traffic, open(tpath, "w"), indent=1)
+    print(f"wrote profiles/{name}; traffic[{key}]: " +
+          ", ".join(f"{r} {rec[r]['bytes'] / 1e9:.2f} GB" for r in ("up_gemm", "down_gemm") if r in rec))
+
+
+if __name__ == "__main__":
+    main()
