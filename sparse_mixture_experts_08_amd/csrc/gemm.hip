@@ -14,11 +14,16 @@
 //   down : A = h rows (already in sorted order), B = W2 rows, epilogue y_rows = round(acc).
 // Empty experts create no tiles and read no weights.
 //
-// Data path.  A and B tiles are staged through LDS in 128-byte-per-row K stages (global loads into
-// registers one stage ahead; one or two LDS buffers; 16-byte chunks XOR-swizzled by row), fragments
-// read with 16-byte LDS reads.  MFMA per element type:
+// Data path.  A and B tiles are staged through LDS in 128-byte-per-row K stages (16-byte chunks
+// XOR-swizzled by row) and read back as MFMA fragments with 16-byte LDS reads.  Three kernels:
+//   grouped_gemm_kernel    : global loads into registers one stage ahead, then LDS stores (16-row decode
+//                            tiles of every dtype; fp32 128-row tiles);
+//   grouped_gemm_w_kernel  : bf16 128/256-row tiles, one 128 x 128 block of 32x32 MFMAs per wavefront,
+//                            stages copied global -> LDS by direct-to-LDS loads;
+//   grouped_gemm_f8_kernel : fp8 128-row tiles, direct-to-LDS staging of the operands and their scales.
+// MFMA per element type:
 //   fp32 : v_mfma_f32_16x16x4_f32   (4 per 16-byte fragment; lane group q holds k = 4q + e)
-//   bf16 : v_mfma_f32_16x16x32_bf16 (one per 16-byte fragment)
+//   bf16 : v_mfma_f32_16x16x32_bf16 (one per 16-byte fragment), v_mfma_f32_32x32x16_bf16 (wide kernel)
 //   fp8  : v_mfma_scale_f32_16x16x128_f8f6f4 with unit exponent scales, one per 128-byte stage, whose
 //          fp32 result is multiplied by (activation scale of the row) * (weight block scale) and
 //          added to the accumulator: a 128-wide K stage is exactly one 128x128 weight block.
