@@ -745,9 +745,78 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
         }
 }
 
+// One 128-wide K stage of fp8 MFMAs for the direct-to-LDS fp8 kernel: the wavefront's WM x WN blocks of
+// 16 x 16 (and the W3 half for the up GEMM).  Same arithmetic as mma_stage's fp8 path, in a schedule that
+// keeps the register footprint fixed: B fragments of the stage stay in registers, A fragments and the
+// row scales are read one row block ahead; with more than 64 accumulator VGPRs a row block's MFMAs also
+// wait for the rescaling of the previous block's results, so only one block's MFMA results are live and
+// a 128 x 64 wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.
+template <bool UP, int WM, int WN, int BN>
+__device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_lds, const float* sA_lds, float sb1,
+                                       float sb3, int wm0, int wn0, int lane, f32x4 (&acc1)[WM][WN],
+                                       f32x4 (&acc3)[WM][WN])
+{
+    const int r16 = lane & 15, q = lane >> 4;
+    constexpr bool TIGHT = WM * WN * (UP ? 2 : 1) > 16;  // more than 64 accumulator VGPRs
+    auto frag = [&](const uint8_t* base, int row) {
+        const i32x4 lo = *(const i32x4*)(base + swz(row, 2 * q));
+        const i32x4 hi = *(const i32x4*)(base + swz(row, 2 * q + 1));
+        return (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    i32x8 b1[WN], b3[UP ? WN : 1];
+#pragma unroll
+    for (int j = 0; j < WN; j++) {
+        b1[j] = frag(Bs_lds, wn0 + j * 16 + r16);
+        if constexpr (UP) b3[j] = frag(Bs_lds, BN + wn0 + j * 16 + r16);
+    }
+    // row scales of the lane's four rows 4q .. 4q + 3 of row block i (16-byte aligned)
+    auto scales = [&](int i) { return *(const f32x4*)(sA_lds + wm0 + i * 16 + 4 * q); };
+    i32x8 a = frag(As_lds, wm0 + r16);
+    f32x4 sa = scales(0);
+#pragma unroll
+    for (int i = 0; i < WM; i++) {
+        i32x8 a_next = a;
+        f32x4 sa_next = sa;
+        if (i + 1 < WM) {
+            a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
+            sa_next = scales(i + 1);
+        }
+        float s1[4], s3[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            s1[r] = sa[r] * sb1;
+            s3[r] = sa[r] * sb3;
+        }
+#pragma unroll
+        for (int j = 0; j < WN; j++) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b1[j], zero, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc1[i][j][r] += p1[r] * s1[r];
+            if constexpr (UP) {
+                const f32x4 p3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * s3[r];
+            }
+        }
+        // The next row block's operands pass through an empty asm that also takes this block's rescaled
+        // accumulators, so its MFMAs cannot be issued before this block's results are consumed: only one
+        // block's MFMA results are live at a time.
+        if constexpr (TIGHT) {
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                if constexpr (UP) asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i][j]), "v"(acc3[i][j]));
+                else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i][j]));
+            }
+        }
+        a = a_next;
+        sa = sa_next;
+    }
+}
+
 // ---------------------------------------------------------------------------------------------------
-// fp8 form with direct-to-LDS staging (128-row tiles, eight wavefronts as 2 x 4, the 16x16x128 fp8 MFMA
-// and per-K-block rescaling of mma_stage).  A K stage is 128 fp8 elements: one 128-byte line of every A
+// fp8 form with direct-to-LDS staging (128- or 256-row tiles, eight wavefronts as 2 x 4, the 16x16x128
+// fp8 MFMA and per-K-block rescaling of mma_f8).  A K stage is 128 fp8 elements: one 128-byte line of every A
 // row, W1 row and W3 row, stored as in grouped_gemm_kernel (16-byte chunks XOR-swizzled by row), so
 // mma_stage reads it unchanged.  The stages sit in a ring of NSTG buffers filled by global_load_lds (no
 // staging registers, no LDS stores), NSTG - 1 of them in flight while one is computed.  The scales of a
@@ -755,10 +824,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
 // row), wavefront 2 the W1 block scales, wavefront 3 the W3 block scales, the others a dummy copy, so
 // every wavefront issues the same number of loads per stage and one vmcnt value waits for a stage.
 // ---------------------------------------------------------------------------------------------------
-template <bool UP, int BN, int NSTG>
+template <bool UP, int BM, int BN, int NSTG>
 __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
 {
-    constexpr int BM = 128, WAVES_M = 2, WAVES_N = 4, NW = 8, NT = 512;
+    constexpr int WAVES_M = 2, WAVES_N = 4, NW = 8, NT = 512;
     constexpr int WM = BM / 16 / WAVES_M, WN = BN / 16 / WAVES_N;
     constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
     constexpr int ROWS = BM + NB;                      // 128-byte LDS rows per stage
@@ -772,6 +841,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     static_assert(WN * 16 <= 128 && 128 % (WN * 16) == 0, "a wavefront's columns share one fp8 block scale");
     static_assert((NSTG - 1) * NL < 64, "vmcnt range");
     static_assert(!UP || BM * BN * 4 <= NSTG * STAGE, "h tile must fit the ring");
+    static_assert(BM == 128 || BM == 256, "128- or 256-row tiles");
+    constexpr int SW = BM / 64;                        // wavefronts copying A row scales; W1, W3 next
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STAGE];
     __shared__ __attribute__((aligned(256))) float scl[NSTG][NW * 64];   // per stage: A row scales, W1, W3 block scales
@@ -815,8 +886,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     }
     // scale copy of this wavefront: byte offset from its base, the base moved by the K stage below
     uint32_t soff = 0;
-    if (wave < 2) soff = (uint32_t)s_tok[wave * 64 + lane] * (uint32_t)g.ldas * 4u;
-    else if (wave == 2 || (UP && wave == 3)) soff = (uint32_t)(lane < BN / 128 ? lane : 0) * (uint32_t)nkb * 4u;
+    if (wave < SW) soff = (uint32_t)s_tok[wave * 64 + lane] * (uint32_t)g.ldas * 4u;
+    else if (wave == SW || (UP && wave == SW + 1)) soff = (uint32_t)(lane < BN / 128 ? lane : 0) * (uint32_t)nkb * 4u;
 
     const int nstages = K / 128;
     const int kshift = (nb * g.krot) % nstages;
@@ -827,9 +898,9 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
         const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
 #pragma unroll
         for (int p = 0; p < PERW; p++) dma16((p < PA ? g.A : p < PA + PB1 ? W1 : W3) + koff, off[p], dst + p * NW * 1024);
-        const uint8_t* sb = wave < 2 ? (const uint8_t*)(g.As + ks)
-                          : wave == 2 ? (const uint8_t*)(W1s + ks)
-                          : (UP && wave == 3) ? (const uint8_t*)(W3s + ks) : (const uint8_t*)W1s;
+        const uint8_t* sb = wave < SW ? (const uint8_t*)(g.As + ks)
+                          : wave == SW ? (const uint8_t*)(W1s + ks)
+                          : (UP && wave == SW + 1) ? (const uint8_t*)(W3s + ks) : (const uint8_t*)W1s;
         dma4(sb, soff, scl0 + (buf * NW * 64 + wave * 64) * 4);
     };
 
@@ -848,8 +919,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     for (int s = 0; s < nstages; s++) {
         const float* sc = scl[buf];
         const uint8_t* st = ring + buf * STAGE;
-        mma_stage<ET_FP8, UP, WM, WN, BN>(st, st + BM * 128, sc, sc[128 + cb], UP ? sc[192 + cb] : 0.f, wm0, wn0,
-                                         lane, acc1, acc3);
+        mma_f8<UP, WM, WN, BN>(st, st + BM * 128, sc, sc[BM + cb], UP ? sc[BM + 64 + cb] : 0.f, wm0, wn0, lane, acc1,
+                               acc3);
         if (s + 1 < nstages) {
             wait_vmcnt<(NSTG - 2) * NL>();             // stage s + 1 has landed
             lds_barrier();                             // ... for every wavefront; stage s is read
@@ -938,15 +1009,18 @@ static void launch_w(GemmArgs a, hipStream_t stream)
 #ifndef MOE_F8_NSTG
 #define MOE_F8_NSTG 3
 #endif
+#ifndef MOE_F8_256_DN_BN
+#define MOE_F8_256_DN_BN 256
+#endif
 // 1: fp8 GEMMs with 128-row tiles use grouped_gemm_f8_kernel (direct-to-LDS staging).
 #ifndef MOE_F8_DMA
 #define MOE_F8_DMA 1
 #endif
-template <bool UP, int BN>
+template <bool UP, int BM, int BN>
 static void launch_f8(GemmArgs a, hipStream_t stream)
 {
     const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
-    grouped_gemm_f8_kernel<UP, BN, MOE_F8_NSTG><<<(unsigned)nblk, 512, 0, stream>>>(a);
+    grouped_gemm_f8_kernel<UP, BM, BN, BM == 128 ? MOE_F8_NSTG : 2><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
 
 // 1: bf16 up GEMMs with 128-row tiles use grouped_gemm_w_kernel when inter and the shared width are
@@ -1089,7 +1163,8 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     if (fp8) {
         up.n_blocks = (int)(ws.inter_max / 128);
         if (bm == 16) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
-        else if (MOE_F8_DMA) launch_f8<true, 128>(up, stream);
+        else if (bm == 256) launch_f8<true, 256, 128>(up, stream);
+        else if (MOE_F8_DMA) launch_f8<true, 128, 128>(up, stream);
         else launch_one<ET_FP8, true, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(up, stream);
     } else if (f32) {
         up.n_blocks = (int)(ws.inter_max / 64);
@@ -1151,15 +1226,19 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     } else if (s.d % 256) {
         // d an odd multiple of 128: 128-wide n-blocks (the wider configurations need d % 256 == 0)
         dn.n_blocks = (int)(s.d / 128);
-        if (fp8 && MOE_F8_DMA) launch_f8<false, 128>(dn, stream);
+        if (fp8 && bm == 256) launch_f8<false, 256, 128>(dn, stream);
+        else if (fp8 && MOE_F8_DMA) launch_f8<false, 128, 128>(dn, stream);
         else if (fp8) launch_one<ET_FP8, false, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
         else if (f32) launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
         else if (bm == 128) launch_one<ET_BF16, false, true, 128, 128, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(dn, stream);
         else launch_one<ET_BF16, false, true, 256, 128, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(dn, stream);
+    } else if (fp8 && bm == 256) {
+        dn.n_blocks = (int)(s.d / MOE_F8_256_DN_BN);
+        launch_f8<false, 256, MOE_F8_256_DN_BN>(dn, stream);
     } else if (bm == 128) {
         if (fp8) {
             dn.n_blocks = (int)(s.d / MOE_FP8_DN_BN);
-            if (MOE_F8_DMA) launch_f8<false, MOE_FP8_DN_BN>(dn, stream);
+            if (MOE_F8_DMA) launch_f8<false, 128, MOE_FP8_DN_BN>(dn, stream);
             else launch_one<ET_FP8, false, true, 128, MOE_FP8_DN_BN, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
         } else if (f32) {
             dn.n_blocks = (int)(s.d / 128);

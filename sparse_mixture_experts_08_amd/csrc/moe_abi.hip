@@ -13,6 +13,12 @@ namespace moe {
 #ifndef MOE_T256_MIN
 #define MOE_T256_MIN 24
 #endif
+#ifndef MOE_FP8_MAX_TILE_ROWS
+#define MOE_FP8_MAX_TILE_ROWS 256
+#endif
+#ifndef MOE_FP8_T256_MIN
+#define MOE_FP8_T256_MIN 192
+#endif
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -21,11 +27,12 @@ int tile_rows(const moe_shape_t& s)
     // By the average rows per routed expert: decode-sized groups (<= 24 rows) -> 16-row tiles (weight
     // streaming).  Otherwise bf16 takes 256-row tiles: an expert of up to 256 rows reads its weights once,
     // and a 256 x 256 output block needs fewer staged bytes per MFMA than 128 x 512; row blocks past a
-    // tile's end are skipped.  fp8 and fp32 keep 128: the fp8 per-K-block scaling accumulates in VGPRs,
-    // which caps the per-wave tile.
+    // tile's end are skipped.  fp8 takes 256-row tiles above 192 rows per expert (fewer staged bytes and
+    // LDS fragment reads per MFMA), else 128; fp32 keeps 128.
     const int64_t per_expert = s.T * s.k / (s.E > 0 ? s.E : 1);
     if (per_expert <= 24) return 16;
-    if (per_expert <= MOE_T256_MIN || s.act_dtype == MOE_F32 || s.w_dtype == MOE_FP8_E4M3) return 128;
+    if (s.w_dtype == MOE_FP8_E4M3) return per_expert > MOE_FP8_T256_MIN ? MOE_FP8_MAX_TILE_ROWS : 128;
+    if (per_expert <= MOE_T256_MIN || s.act_dtype == MOE_F32) return 128;
     return MOE_MAX_TILE_ROWS;
 }
 

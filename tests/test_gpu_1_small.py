@@ -1,4 +1,4 @@
-"""GPU parity on shapes the oracle finishes in seconds: every tile path (16- and 128-row tiles), every
+"""GPU parity on shapes the oracle finishes in seconds: every tile path (16-, 128- and 256-row tiles), every
 dtype pair, ragged tails, and the degenerate cases of the method.  All calls go through the C ABI."""
 import numpy as np
 import pytest
@@ -21,6 +21,8 @@ SMALL = [
     W.Workload("small-bf16-bigtile", 1100, 512, 8, 2, 256, 384, BF16, BF16),   # ~275 rows per expert
     W.Workload("small-fp8-decode", 150, 1024, 32, 4, 512, 256, BF16, FP8),
     W.Workload("small-fp8-prefill", 700, 512, 16, 4, 256, 384, BF16, FP8),
+    W.Workload("small-fp8-bigtile", 1100, 512, 8, 2, 256, 384, BF16, FP8),     # 256-row fp8 tiles, ragged
+    W.Workload("small-fp8-d384-bigtile", 500, 384, 4, 2, 256, 256, BF16, FP8),  # ... with d an odd multiple of 128
     W.Workload("small-skew-bf16", 300, 512, 64, 8, 256, 256, BF16, BF16, skew=True),
     W.Workload("tiny-E256-T5", 5, 512, 256, 8, 256, 256, BF16, BF16),     # few tokens over many experts
     W.Workload("small-bf16-d384", 600, 384, 16, 4, 256, 384, BF16, BF16),     # d an odd multiple of 128
