@@ -977,112 +977,43 @@ static void launch_one(GemmArgs a, hipStream_t stream)
         <<<(unsigned)nblk, 64 * WAVES_M * WAVES_N, 0, stream>>>(a);
 }
 
+// K-stage rotation per n-block: the down GEMM (rows of inter elements) and the large-tile up GEMMs gain
+// from it; the up GEMM with 16-row tiles already streams at the HBM ceiling without it.
+#ifndef MOE_KROT_UP16
+#define MOE_KROT_UP16 0
+#endif
+#ifndef MOE_KROT_UP
+#define MOE_KROT_UP 3
+#endif
+#ifndef MOE_KROT_DN
+#define MOE_KROT_DN 1
+#endif
+// Tiles per XCD group of the large-tile block order (see grouped_gemm_kernel).
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 8
+#endif
 
-// Row bytes per K stage and ring depth of grouped_gemm_w_kernel (128-byte rows in a ring of two measured
-// best: 64-byte rows double the L2 requests, and deeper rings of them lose more than they hide).
-#ifndef MOE_W_RB
-#define MOE_W_RB 128
-#endif
-#ifndef MOE_W_NSTG
-#define MOE_W_NSTG 2
-#endif
-#ifndef MOE_W256_RB
-#define MOE_W256_RB 128
-#endif
-#ifndef MOE_W256_NSTG
-#define MOE_W256_NSTG 2
-#endif
-#ifndef MOE_KROT_W
-#define MOE_KROT_W 3
-#endif
-template <bool UP, int BM>
+// bf16 256-row tiles: 128-byte K stages in a ring of two (64-byte stages in deeper rings request twice
+// the lines and measured slower).  Both GEMMs walk K with the up GEMM's rotation here (other rotations
+// measured no different).
+template <bool UP>
 static void launch_w(GemmArgs a, hipStream_t stream)
 {
-    a.krot = MOE_KROT_W;
+    a.krot = MOE_KROT_UP;
     const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
-    if constexpr (BM == 128)
-        grouped_gemm_w_kernel<UP, BM, MOE_W_RB, MOE_W_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
-    else
-        grouped_gemm_w_kernel<UP, BM, MOE_W256_RB, MOE_W256_NSTG><<<(unsigned)nblk, 256, 0, stream>>>(a);
+    grouped_gemm_w_kernel<UP, 256, 128, 2><<<(unsigned)nblk, 256, 0, stream>>>(a);
 }
 
-#ifndef MOE_F8_NSTG
-#define MOE_F8_NSTG 3
-#endif
-#ifndef MOE_F8_256_DN_BN
-#define MOE_F8_256_DN_BN 256
-#endif
-// 1: fp8 GEMMs with 128-row tiles use grouped_gemm_f8_kernel (direct-to-LDS staging).
-#ifndef MOE_F8_DMA
-#define MOE_F8_DMA 1
-#endif
+// fp8 tiles of 128 or 256 rows: a ring of three stages for 128-row tiles, two for 256 (LDS).
 template <bool UP, int BM, int BN>
 static void launch_f8(GemmArgs a, hipStream_t stream)
 {
     const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
-    grouped_gemm_f8_kernel<UP, BM, BN, BM == 128 ? MOE_F8_NSTG : 2><<<(unsigned)nblk, 512, 0, stream>>>(a);
+    grouped_gemm_f8_kernel<UP, BM, BN, BM == 128 ? 3 : 2><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
 
-// 1: bf16 up GEMMs with 128-row tiles use grouped_gemm_w_kernel when inter and the shared width are
-// multiples of 256, and 256-row tiles use it for both GEMMs.  MOE_LARGE_W_DN = 1 also sends the down
-// GEMM of 128-row tiles there when d is a multiple of 512 (measured slightly slower than
-// grouped_gemm_kernel on MI355X, so off by default).
-#ifndef MOE_LARGE_W
-#define MOE_LARGE_W 1
-#endif
-#ifndef MOE_LARGE_W_DN
-#define MOE_LARGE_W_DN 0
-#endif
-
-// Output features per block for the 128- and 256-row tile classes.
-#ifndef MOE_MID_UP_BN
-#define MOE_MID_UP_BN 128
-#endif
-#ifndef MOE_MID_DN_BN
-#define MOE_MID_DN_BN 256
-#endif
-#ifndef MOE_MID_NBUF
-#define MOE_MID_NBUF 1
-#endif
-#ifndef MOE_MID_MINW
-#define MOE_MID_MINW 2
-#endif
-#ifndef MOE_GROUP_M
-#define MOE_GROUP_M 8
-#endif
-#ifndef MOE_GROUP_M_256
-#define MOE_GROUP_M_256 8
-#endif
-#ifndef MOE_FP8_WM
-#define MOE_FP8_WM 2
-#endif
-#ifndef MOE_FP8_WN
-#define MOE_FP8_WN 4
-#endif
-#ifndef MOE_FP8_NBUF
-#define MOE_FP8_NBUF 2
-#endif
-#ifndef MOE_FP8_MINW
-#define MOE_FP8_MINW 2
-#endif
-#ifndef MOE_FP8_DN_BN
-#define MOE_FP8_DN_BN 256
-#endif
-#ifndef MOE_BIG_WM
-#define MOE_BIG_WM 2
-#endif
-#ifndef MOE_BIG_WN
-#define MOE_BIG_WN 2
-#endif
-#ifndef MOE_BIG_MINW
-#define MOE_BIG_MINW 1
-#endif
-#ifndef MOE_BIG_DN_BN
-#define MOE_BIG_DN_BN 256
-#endif
-
-// 16-row tiles, up GEMM (bf16): output features (of W1 and of W3) per block, wavefronts, minimum
-// wavefronts per SIMD.  inter and inter_shared must be multiples of MOE_SMALL_UP_BN.
+// 16-row tiles (bf16): output features per block, wavefronts, minimum wavefronts per SIMD.  inter and
+// inter_shared must be multiples of MOE_SMALL_UP_BN.
 #ifndef MOE_SMALL_UP_BN
 #define MOE_SMALL_UP_BN 64
 #endif
@@ -1092,7 +1023,6 @@ static void launch_f8(GemmArgs a, hipStream_t stream)
 #ifndef MOE_SMALL_UP_MINW
 #define MOE_SMALL_UP_MINW 1
 #endif
-// 16-row tiles, down GEMM (bf16): output features per block, wavefronts, minimum wavefronts per SIMD.
 #ifndef MOE_SMALL_DN_BN
 #define MOE_SMALL_DN_BN 64
 #endif
@@ -1101,18 +1031,6 @@ static void launch_f8(GemmArgs a, hipStream_t stream)
 #endif
 #ifndef MOE_SMALL_DN_MINW
 #define MOE_SMALL_DN_MINW 1
-#endif
-
-// K-stage rotation per n-block: the down GEMM (rows of inter elements) and the up GEMM with 128-row
-// tiles gain from it; the up GEMM with 16-row tiles already streams at the HBM ceiling without it.
-#ifndef MOE_KROT_UP16
-#define MOE_KROT_UP16 0
-#endif
-#ifndef MOE_KROT_UP
-#define MOE_KROT_UP 3
-#endif
-#ifndef MOE_KROT_DN
-#define MOE_KROT_DN 1
 #endif
 
 // Common fields of both GEMMs' arguments.
@@ -1124,10 +1042,16 @@ static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws, int e_base)
     a.ntiles = ws.sync;
     a.max_tiles = (int)ws.max_tiles;
     a.E = (int)s.E;
-    a.group_m = tile_rows(s) == 16 ? 0 : tile_rows(s) == 256 ? MOE_GROUP_M_256 : MOE_GROUP_M;
+    a.group_m = tile_rows(s) == 16 ? 0 : MOE_GROUP_M;
     return a;
 }
 
+// Kernel per (dtype, tile rows):
+//   16-row tiles          grouped_gemm_kernel (register-staged), every dtype
+//   fp32, 128-row tiles   grouped_gemm_kernel
+//   bf16, 256-row tiles   grouped_gemm_w_kernel; the down GEMM with d an odd multiple of 128 takes
+//                         grouped_gemm_kernel with 128-wide n-blocks
+//   fp8, 128/256-row      grouped_gemm_f8_kernel
 hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, const void* W3, const float* W1s,
                           const float* W3s, const void* S1, const void* S3, const float* S1s, const float* S3s,
                           const Workspace& ws, hipStream_t stream, int e_base, int n_shared)
@@ -1163,30 +1087,18 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     if (fp8) {
         up.n_blocks = (int)(ws.inter_max / 128);
         if (bm == 16) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
-        else if (bm == 256) launch_f8<true, 256, 128>(up, stream);
-        else if (MOE_F8_DMA) launch_f8<true, 128, 128>(up, stream);
-        else launch_one<ET_FP8, true, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(up, stream);
+        else if (bm == 128) launch_f8<true, 128, 128>(up, stream);
+        else launch_f8<true, 256, 128>(up, stream);
     } else if (f32) {
         up.n_blocks = (int)(ws.inter_max / 64);
         if (bm == 16) launch_one<ET_F32, true, false, 16, 64, 1, 4>(up, stream);
         else launch_one<ET_F32, true, false, 128, 64, 2, 2>(up, stream);
+    } else if (bm == 16) {
+        up.n_blocks = (int)(ws.inter_max / MOE_SMALL_UP_BN);
+        launch_one<ET_BF16, true, true, 16, MOE_SMALL_UP_BN, 1, MOE_SMALL_UP_WAVES, 2, MOE_SMALL_UP_MINW>(up, stream);
     } else {
-        if (bm == 16) {
-            up.n_blocks = (int)(ws.inter_max / MOE_SMALL_UP_BN);
-            launch_one<ET_BF16, true, true, 16, MOE_SMALL_UP_BN, 1, MOE_SMALL_UP_WAVES, 2, MOE_SMALL_UP_MINW>(up, stream);
-        } else if (bm == 128 && MOE_LARGE_W && s.inter % 256 == 0 && n_shared % 256 == 0) {
-            up.n_blocks = (int)(ws.inter_max / 256);
-            launch_w<true, 128>(up, stream);
-        } else if (bm == 128) {
-            up.n_blocks = (int)(ws.inter_max / MOE_MID_UP_BN);
-            launch_one<ET_BF16, true, true, 128, MOE_MID_UP_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(up, stream);
-        } else if (MOE_LARGE_W) {
-            up.n_blocks = (int)(ws.inter_max / 128);
-            launch_w<true, 256>(up, stream);
-        } else {
-            up.n_blocks = (int)(ws.inter_max / 128);
-            launch_one<ET_BF16, true, true, 256, 128, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(up, stream);
-        }
+        up.n_blocks = (int)(ws.inter_max / 128);
+        launch_w<true>(up, stream);
     }
     return hipGetLastError();
 }
@@ -1215,6 +1127,8 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     dn.K_s = n_shared;
     dn.krot = MOE_KROT_DN;
     const int bm = tile_rows(s);
+    // 256-wide n-blocks where d allows (d is a multiple of 128; an odd multiple takes 128-wide ones)
+    const bool wide = s.d % 256 == 0;
     if (bm == 16) {
         dn.n_blocks = (int)(s.d / 64);
         if (fp8) launch_one<ET_FP8, false, true, 16, 64, 1, 4>(dn, stream);
@@ -1223,39 +1137,19 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
             dn.n_blocks = (int)(s.d / MOE_SMALL_DN_BN);
             launch_one<ET_BF16, false, true, 16, MOE_SMALL_DN_BN, 1, MOE_SMALL_DN_WAVES, 2, MOE_SMALL_DN_MINW>(dn, stream);
         } else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
-    } else if (s.d % 256) {
-        // d an odd multiple of 128: 128-wide n-blocks (the wider configurations need d % 256 == 0)
+    } else if (fp8) {
+        dn.n_blocks = (int)(s.d / (wide ? 256 : 128));
+        if (bm == 128) wide ? launch_f8<false, 128, 256>(dn, stream) : launch_f8<false, 128, 128>(dn, stream);
+        else wide ? launch_f8<false, 256, 256>(dn, stream) : launch_f8<false, 256, 128>(dn, stream);
+    } else if (f32) {
         dn.n_blocks = (int)(s.d / 128);
-        if (fp8 && bm == 256) launch_f8<false, 256, 128>(dn, stream);
-        else if (fp8 && MOE_F8_DMA) launch_f8<false, 128, 128>(dn, stream);
-        else if (fp8) launch_one<ET_FP8, false, true, 128, 128, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
-        else if (f32) launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
-        else if (bm == 128) launch_one<ET_BF16, false, true, 128, 128, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(dn, stream);
-        else launch_one<ET_BF16, false, true, 256, 128, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(dn, stream);
-    } else if (fp8 && bm == 256) {
-        dn.n_blocks = (int)(s.d / MOE_F8_256_DN_BN);
-        launch_f8<false, 256, MOE_F8_256_DN_BN>(dn, stream);
-    } else if (bm == 128) {
-        if (fp8) {
-            dn.n_blocks = (int)(s.d / MOE_FP8_DN_BN);
-            if (MOE_F8_DMA) launch_f8<false, 128, MOE_FP8_DN_BN>(dn, stream);
-            else launch_one<ET_FP8, false, true, 128, MOE_FP8_DN_BN, MOE_FP8_WM, MOE_FP8_WN, MOE_FP8_NBUF, MOE_FP8_MINW>(dn, stream);
-        } else if (f32) {
-            dn.n_blocks = (int)(s.d / 128);
-            launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
-        } else if (MOE_LARGE_W && MOE_LARGE_W_DN && s.d % 512 == 0) {
-            dn.n_blocks = (int)(s.d / 512);
-            launch_w<false, 128>(dn, stream);
-        } else {
-            dn.n_blocks = (int)(s.d / MOE_MID_DN_BN);
-            launch_one<ET_BF16, false, true, 128, MOE_MID_DN_BN, 2, 2, MOE_MID_NBUF, MOE_MID_MINW>(dn, stream);
-        }
-    } else if (MOE_LARGE_W) {
+        launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
+    } else if (wide) {
         dn.n_blocks = (int)(s.d / 256);
-        launch_w<false, 256>(dn, stream);
+        launch_w<false>(dn, stream);
     } else {
-        dn.n_blocks = (int)(s.d / MOE_BIG_DN_BN);
-        launch_one<ET_BF16, false, true, 256, MOE_BIG_DN_BN, MOE_BIG_WM, MOE_BIG_WN, 2, MOE_BIG_MINW>(dn, stream);
+        dn.n_blocks = (int)(s.d / 128);
+        launch_one<ET_BF16, false, true, 256, 128, 2, 2, 2, 1>(dn, stream);
     }
     return hipGetLastError();
 }

@@ -7,19 +7,6 @@
 
 namespace moe {
 
-#ifndef MOE_MAX_TILE_ROWS
-#define MOE_MAX_TILE_ROWS 256
-#endif
-#ifndef MOE_T256_MIN
-#define MOE_T256_MIN 24
-#endif
-#ifndef MOE_FP8_MAX_TILE_ROWS
-#define MOE_FP8_MAX_TILE_ROWS 256
-#endif
-#ifndef MOE_FP8_T256_MIN
-#define MOE_FP8_T256_MIN 192
-#endif
-
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int tile_rows(const moe_shape_t& s)
@@ -31,9 +18,9 @@ int tile_rows(const moe_shape_t& s)
     // LDS fragment reads per MFMA), else 128; fp32 keeps 128.
     const int64_t per_expert = s.T * s.k / (s.E > 0 ? s.E : 1);
     if (per_expert <= 24) return 16;
-    if (s.w_dtype == MOE_FP8_E4M3) return per_expert > MOE_FP8_T256_MIN ? MOE_FP8_MAX_TILE_ROWS : 128;
-    if (per_expert <= MOE_T256_MIN || s.act_dtype == MOE_F32) return 128;
-    return MOE_MAX_TILE_ROWS;
+    if (s.w_dtype == MOE_FP8_E4M3) return per_expert > 192 ? 256 : 128;
+    if (s.act_dtype == MOE_F32) return 128;
+    return 256;
 }
 
 Workspace carve_workspace(const moe_shape_t& s, void* base)
