@@ -534,34 +534,37 @@ __device__ __forceinline__ bool block_work(const GemmArgs& g, int& tile, int& nb
 }
 
 // ---------------------------------------------------------------------------------------------------
-// Wide form for bf16 tiles of BM = 128 or 256 rows: each wavefront owns a 128 x 128 output block (UP:
-// 64 columns of W1 and the same 64 of W3) held in 16 accumulators of 32 x 32 (v_mfma_f32_32x32x16_bf16),
-// which needs the register file of one wavefront per SIMD.  Against a 64 x 128 block this cuts the LDS
-// bytes read per MFMA by a third.  Four wavefronts: BM = 128 -> 1 x 4 (block 128 x 512 output columns:
-// half the n-blocks of a 128 x 256 block, so x rows are fetched half as often), BM = 256 -> 2 x 2.
+// Wide form for bf16 tiles of BM = 128 or 256 rows, v_mfma_f32_32x32x16_bf16.  NW = 4: one wavefront
+// per SIMD owning a 128 x 128 output block (UP: 64 columns of W1 and the same 64 of W3) in 16 accumulators
+// of 32 x 32 (BM = 128 -> 1 x 4 wavefronts, BM = 256 -> 2 x 2).  NW = 8 (used: BM = 256): the same
+// 256 x 256 block tile as 2 x 4 wavefronts of 128 x 64, two per SIMD, so one wavefront issues MFMAs
+// while the other waits on a fragment read or the stage barrier (skewed workload 16.2 -> 15.1 ms).
 // K stages of RB / 2 elements in a ring of NSTG, copied by direct-to-LDS loads; at the end of each stage
 // the barrier publishing the next stage, the refill of the freed buffer and the first fragment reads of
 // the next stage sit under the MFMAs of the stage's last K step.  With whole-line (128-byte) rows the
-// time of this kernel on MI355X is set by the global -> LDS copies (the same loop without MFMAs takes
-// 85-95 % of it), chiefly by the L2 misses of the weight panels and gathered x rows.
+// time of this kernel on MI355X is set mostly by the global -> LDS copies (the same loop without MFMAs
+// takes about 80 % of it, without the copies about 60 %): the per-CU rate of L2 line requests, hit or
+// miss, not HBM bandwidth, which is why the block tile is as large as the register file allows.
 // ---------------------------------------------------------------------------------------------------
-template <bool UP, int BM, int RB, int NSTG>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
+template <bool UP, int BM, int RB, int NSTG, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 {
-    constexpr int WAVES_M = BM / 128, WAVES_N = 4 / WAVES_M;
-    constexpr int NJ = UP ? 2 : 4;                     // 32-column MFMA blocks per half (UP) or per wavefront
+    constexpr int WAVES_M = BM / 128, WAVES_N = NW / WAVES_M;
+    constexpr int NJ = (UP ? 2 : 4) * 4 / NW;          // 32-column MFMA blocks per half (UP) or per wavefront
     constexpr int WCOL = 32 * NJ;                      // wavefront columns (per half for UP)
     constexpr int BN = WAVES_N * WCOL;                  // block columns (per half for UP)
     constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
     constexpr int ROWS = BM + NB;
     constexpr int STAGE = ROWS * RB;
     constexpr int CPR = RB / 16, RPL = 64 / CPR;       // 16-byte chunks per row, rows per 1-KB load
-    constexpr int PERW = ROWS / RPL / 4;               // 1-KB loads per wavefront per stage
-    constexpr int PA = BM / RPL / 4, PB1 = BN / RPL / 4; // ... of which A rows, W1 (or W2) rows
+    constexpr int PERW = ROWS / RPL / NW;              // 1-KB loads per wavefront per stage
+    constexpr int PA = BM / RPL / NW, PB1 = BN / RPL / NW; // ... of which A rows, W1 (or W2) rows
     constexpr int KS = RB / 32;                        // 16-element K steps per stage
     static_assert(BM == 128 || BM == 256, "128- or 256-row tiles");
     static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
-    static_assert(ROWS % (4 * RPL) == 0 && (NSTG - 1) * PERW < 64, "loads per wavefront, vmcnt range");
+    static_assert(ROWS % (NW * RPL) == 0 && BM % (NW * RPL) == 0 && BN % (NW * RPL) == 0 && (NSTG - 1) * PERW < 64,
+                  "whole loads per wavefront, vmcnt range");
+    static_assert(NJ >= 1, "at least one 32-column block per wavefront");
     static_assert(BM * 4 <= STAGE, "row table fits the first stage buffer");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STAGE];
@@ -589,7 +592,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
     uint32_t off[PERW];
 #pragma unroll
     for (int p = 0; p < PERW; p++) {
-        const int row = (4 * p + wave) * RPL + lane / CPR;
+        const int row = (NW * p + wave) * RPL + lane / CPR;
         const int lc = (swzr<RB>(row, lane % CPR) - row * RB) >> 4;  // logical chunk stored at chunk lane % CPR
         if (p < PA) off[p] = (uint32_t)s_tok[row] * (uint32_t)g.lda + lc * 16;
         else if (p < PA + PB1) off[p] = (uint32_t)(n0 + row - BM) * (uint32_t)ldb + lc * 16;
@@ -617,8 +620,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_w_kernel(GemmArgs g)
         const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
 #pragma unroll
         for (int p = 0; p < PERW; p++) {
-            if (p < PA && (4 * p + wave) * RPL >= a_rows) continue;
-            dma16(p < PA ? a : p < PA + PB1 ? b1 : b3, off[p], dst + p * 4096);
+            if (p < PA && (NW * p + wave) * RPL >= a_rows) continue;
+            dma16(p < PA ? a : p < PA + PB1 ? b1 : b3, off[p], dst + p * NW * 1024);
         }
     };
 
@@ -994,14 +997,15 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 #endif
 
 // bf16 256-row tiles: 128-byte K stages in a ring of two (64-byte stages in deeper rings request twice
-// the lines and measured slower).  Both GEMMs walk K with the up GEMM's rotation here (other rotations
+// the lines and measured slower), eight wavefronts (four, one per SIMD with 128 x 128 each, measured
+// 7 % slower on the skewed workload).  Both GEMMs walk K with the up GEMM's rotation here (other rotations
 // measured no different).
 template <bool UP>
 static void launch_w(GemmArgs a, hipStream_t stream)
 {
     a.krot = MOE_KROT_UP;
     const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
-    grouped_gemm_w_kernel<UP, 256, 128, 2><<<(unsigned)nblk, 256, 0, stream>>>(a);
+    grouped_gemm_w_kernel<UP, 256, 128, 2, 8><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
 
 // fp8 tiles of 128 or 256 rows: a ring of three stages for 128-row tiles, two for 256 (LDS).
