@@ -774,8 +774,63 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
     }
     // row scales of the lane's four rows 4q .. 4q + 3 of row block i (16-byte aligned)
     auto scales = [&](int i) { return *(const f32x4*)(sA_lds + wm0 + i * 16 + 4 * q); };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     i32x8 a = frag(As_lds, wm0 + r16);
     f32x4 sa = scales(0);
+    if constexpr (TIGHT) {
+        // Software pipeline over row blocks: block i's MFMAs are issued before block i - 1's results are
+        // rescaled, so the matrix pipe runs while the vector ALU rescales.  Block i + 1's A operand
+        // passes through an empty asm that also takes block i - 1's rescaled accumulators, so at most
+        // two blocks' MFMA results are live.
+        constexpr int NP = UP ? 2 * WN : WN;          // MFMA results per row block
+        f32x4 pc[NP], pp[NP];
+        float p1s[4], p3s[4];                          // scale products of the previous block
+#pragma unroll
+        for (int i = 0; i <= WM; i++) {
+            i32x8 a_next = a;
+            f32x4 sa_next = sa;
+            if (i < WM) {
+#pragma unroll
+                for (int j = 0; j < WN; j++) {
+                    pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b1[j], zero, 0, 0, 0, 127, 0, 127);
+                    if constexpr (UP)
+                        pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
+                }
+                if (i + 1 < WM) {
+                    a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
+                    sa_next = scales(i + 1);
+                }
+            }
+            if (i > 0) {
+#pragma unroll
+                for (int j = 0; j < WN; j++) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc1[i - 1][j][r] += pp[j][r] * p1s[r];
+                    if constexpr (UP) {
+#pragma unroll
+                        for (int r = 0; r < 4; r++) acc3[i - 1][j][r] += pp[WN + j][r] * p3s[r];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < WN; j++) {
+                    if constexpr (UP) asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i - 1][j]), "v"(acc3[i - 1][j]));
+                    else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i - 1][j]));
+                }
+            }
+            if (i < WM) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    p1s[r] = sa[r] * sb1;
+                    p3s[r] = sa[r] * sb3;
+                }
+#pragma unroll
+                for (int n = 0; n < NP; n++) pp[n] = pc[n];
+                a = a_next;
+                sa = sa_next;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < WM; i++) {
         i32x8 a_next = a;
@@ -792,7 +847,6 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
         }
 #pragma unroll
         for (int j = 0; j < WN; j++) {
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
             const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b1[j], zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
             for (int r = 0; r < 4; r++) acc1[i][j][r] += p1[r] * s1[r];
@@ -800,16 +854,6 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                 const f32x4 p3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
                 for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * s3[r];
-            }
-        }
-        // The next row block's operands pass through an empty asm that also takes this block's rescaled
-        // accumulators, so its MFMAs cannot be issued before this block's results are consumed: only one
-        // block's MFMA results are live at a time.
-        if constexpr (TIGHT) {
-#pragma unroll
-            for (int j = 0; j < WN; j++) {
-                if constexpr (UP) asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i][j]), "v"(acc3[i][j]));
-                else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i][j]));
             }
         }
         a = a_next;
