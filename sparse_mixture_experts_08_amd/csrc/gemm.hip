@@ -533,6 +533,22 @@ __device__ __forceinline__ bool block_work(const GemmArgs& g, int& tile, int& nb
     return true;
 }
 
+// Coalesced store of a block's bf16 output tile: the wavefronts have written it row-major into LDS (row
+// stride OSTR bytes, padded so the two row groups of one LDS write fall on different banks); every
+// thread then copies 16-byte chunks of rows < rows to out (row0 + row, col0 ..), ldo elements apart.
+// Against per-lane 2-byte global stores straight from the accumulators this writes whole lines.
+template <int BM, int OC, int OSTR, int NT>
+__device__ __forceinline__ void store_tile_bf16(const uint8_t* tile, uint8_t* out, int64_t ldo, int row0, int rows,
+                                                int col0)
+{
+    constexpr int CH = OC * 2 / 16;                    // 16-byte chunks per row
+    for (int idx = threadIdx.x; idx < BM * CH; idx += NT) {
+        const int row = idx / CH, ch = idx % CH;
+        if (row < rows)
+            *(uint4*)(out + (((int64_t)row0 + row) * ldo + col0 + ch * 8) * 2) = *(const uint4*)(tile + row * OSTR + ch * 16);
+    }
+}
+
 // ---------------------------------------------------------------------------------------------------
 // Wide form for bf16 tiles of BM = 128 or 256 rows, v_mfma_f32_32x32x16_bf16.  NW = 4: one wavefront
 // per SIMD owning a 128 x 128 output block (UP: 64 columns of W1 and the same 64 of W3) in 16 accumulators
@@ -567,7 +583,9 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
     static_assert(NJ >= 1, "at least one 32-column block per wavefront");
     static_assert(BM * 4 <= STAGE, "row table fits the first stage buffer");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STAGE];
+    constexpr int OSTR = BN * 2 + 16;                  // epilogue: padded LDS row of the block's output tile
+    constexpr int RING = NSTG * STAGE > BM * OSTR ? NSTG * STAGE : BM * OSTR;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
     int* s_tok = (int*)ring;                           // row table, dead before the first load into the ring
 
     int tile, nb;
@@ -727,25 +745,26 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
     case 1: k_loop(IntC<1>{}); break;
     default: k_loop(IntC<0>{}); break;
     }
-    wait_vmcnt<0>();                                   // no load may still target this block's LDS at exit
+    wait_vmcnt<0>();                                   // no load may still target this block's LDS
+    __syncthreads();                                   // every wavefront is done with the ring
 
-    // Epilogue (32x32 accumulator layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4).
+    // Epilogue (32x32 accumulator layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4):
+    // the block's bf16 tile (UP: h = silu(g) * u, BN columns) into LDS, then coalesced to global memory.
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int row = wm0 + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-            if (row >= rows) continue;
-            const int64_t orow = row0 + row;
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
-                const int col = n0 + wn0 + 32 * j + r32;
                 float v;
                 if constexpr (UP) v = silu_mul(round_bf16(acc1[i][j][r]), round_bf16(acc3[i][j][r]));
                 else v = acc1[i][j][r];
-                ((uint16_t*)g.out)[orow * g.ldo + col] = f32_to_bf16(v);
+                *(uint16_t*)(ring + row * OSTR + (wn0 + 32 * j + r32) * 2) = f32_to_bf16(v);
             }
         }
+    __syncthreads();
+    store_tile_bf16<BM, BN, OSTR, 64 * NW>(ring, g.out, g.ldo, row0, rows, n0);
 }
 
 // One 128-wide K stage of fp8 MFMAs for the direct-to-LDS fp8 kernel: the wavefront's WM x WN blocks of
@@ -891,7 +910,9 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     static_assert(BM == 128 || BM == 256, "128- or 256-row tiles");
     constexpr int SW = BM / 64;                        // wavefronts copying A row scales; W1, W3 next
 
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STAGE];
+    constexpr int OSTR = BN * 2 + 16;                  // down epilogue: padded LDS row of the bf16 output tile
+    constexpr int RING = (UP || NSTG * STAGE > BM * OSTR) ? NSTG * STAGE : BM * OSTR;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
     __shared__ __attribute__((aligned(256))) float scl[NSTG][NW * 64];   // per stage: A row scales, W1, W3 block scales
     __shared__ int s_tok[BM];
 
@@ -977,7 +998,22 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     }
     wait_vmcnt<0>();                                   // no load may still target this block's LDS
     lds_barrier();
-    gemm_epilogue<ET_FP8, UP, true, BM, BN, WM, WN, NT>(g, ring, acc1, acc3, rows, row0, n0, wm0, wn0, tid);
+    if constexpr (UP) {
+        gemm_epilogue<ET_FP8, UP, true, BM, BN, WM, WN, NT>(g, ring, acc1, acc3, rows, row0, n0, wm0, wn0, tid);
+    } else {
+        // bf16 output rows through LDS (16x16 layout: lane holds rows 4 (lane / 16) + r, column lane % 16)
+        const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int j = 0; j < WN; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    *(uint16_t*)(ring + (wm0 + i * 16 + 4 * q + r) * OSTR + (wn0 + j * 16 + r16) * 2) =
+                        f32_to_bf16(acc1[i][j][r]);
+        __syncthreads();
+        store_tile_bf16<BM, BN, OSTR, NT>(ring, g.out, g.ldo, row0, rows, n0);
+    }
 }
 
 // fp8 activation quantisation of x: per row, per 128-column group, s = amax / 448 (1 if amax = 0),
