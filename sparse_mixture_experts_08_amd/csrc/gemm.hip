@@ -1211,6 +1211,9 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     dn.K_s = n_shared;
     dn.krot = MOE_KROT_DN;
     const int bm = tile_rows(s);
+    // With at most one tile per expert on average no weight panel is shared between tiles: walk each
+    // tile's n-blocks together instead, so its h rows are fetched once into L2.
+    if (bm > 16 && s.T * s.k <= (int64_t)s.E * bm) dn.group_m = 1;
     // 256-wide n-blocks where d allows (d is a multiple of 128; an odd multiple takes 128-wide ones)
     const bool wide = s.d % 256 == 0;
     if (bm == 16) {

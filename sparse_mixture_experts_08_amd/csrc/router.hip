@@ -13,6 +13,8 @@
 // Top-k.  One wavefront per token; each lane holds E/64 logits as 64-bit keys (order-preserving bits of
 // the logit, then the complemented expert index), so a wave-wide max picks the largest logit and, among
 // equal logits, the lower expert index.  k rounds give the experts in descending-logit order.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "topk.h"
 
@@ -52,6 +54,28 @@ template <> struct X8<float> {
     }
 };
 
+// Four consecutive x elements (8-byte aligned for bf16, 16-byte for fp32).
+template <typename XT> struct X4;
+template <> struct X4<uint16_t> {
+    uint2 r;
+    __device__ __forceinline__ void load(const uint16_t* p) { r = *(const uint2*)p; }
+    __device__ __forceinline__ void get(float* v, bool valid) const
+    {
+        v[0] = valid ? __uint_as_float(r.x << 16) : 0.f;
+        v[1] = valid ? __uint_as_float(r.x & 0xFFFF0000u) : 0.f;
+        v[2] = valid ? __uint_as_float(r.y << 16) : 0.f;
+        v[3] = valid ? __uint_as_float(r.y & 0xFFFF0000u) : 0.f;
+    }
+};
+template <> struct X4<float> {
+    float4 a;
+    __device__ __forceinline__ void load(const float* p) { a = *(const float4*)p; }
+    __device__ __forceinline__ void get(float* v, bool valid) const
+    {
+        v[0] = valid ? a.x : 0.f; v[1] = valid ? a.y : 0.f; v[2] = valid ? a.z : 0.f; v[3] = valid ? a.w : 0.f;
+    }
+};
+
 // Four consecutive elements of one gate row (Wg is [E, d], the gate's nn.Linear weight; rows 16-byte
 // aligned).  Rows past E are clamped to the last row and zeroed at get().
 struct W4 {
@@ -67,33 +91,36 @@ struct W4 {
 };
 
 // Many tokens: L[t][e] = fma chain over i of x[t][i] * Wg[e][i] (+ bias[e]).  Block tile BT (64 or 32)
-// tokens x 64 experts, thread tile 4 x 4, K staged through double-buffered LDS 32 at a time; global
-// loads run two stages ahead of the FMAs (two register sets), so a CU with a single block still
-// covers their latency.  Both tiles are stored K-major ([i][t],
-// [i][e]) so a thread reads four tokens and four experts of one i with two 16-byte reads; the x
-// transposing stores put consecutive lanes on consecutive tokens (conflict-free) and the Wg rows are
-// padded so its transposing stores spread over the banks.  Per output the K loop runs in order: the
-// chain is exactly the contract's.
-template <typename XT, int BT>
-__global__ __launch_bounds__(BT * 4) void router_logits_many_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
-                                                                    const float* __restrict__ bias, float* __restrict__ L,
-                                                                    int T, int d, int E)
+// tokens x 64 experts, thread tile TT (4 or 2) tokens x 4 experts, K staged through double-buffered LDS
+// 32 at a time; global loads run two stages ahead of the FMAs (two register sets), so a CU with a single
+// block still covers their latency.  Both tiles are stored K-major ([i][t], [i][e]) so a thread reads its
+// tokens and four experts of one i with two LDS reads; the x transposing stores put consecutive lanes on
+// consecutive tokens (conflict-free) and the Wg rows are padded so its transposing stores spread over the
+// banks.  Two tokens per thread double the wavefronts of a few-thousand-token call (prefill router
+// 0.42 -> 0.34 ms); four keep more FMAs per LDS read where the wavefronts are plenty.  Per output the K
+// loop runs in order: the chain is exactly the contract's.
+template <typename XT, int BT, int TT>
+__global__ __launch_bounds__(BT / TT * 16) void router_logits_many_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
+                                                                          const float* __restrict__ bias, float* __restrict__ L,
+                                                                          int T, int d, int E)
 {
-    constexpr int BE = 64, BK = 32, WPAD = 4, NT = BT * 4;
+    constexpr int BE = 64, BK = 32, WPAD = 4, NT = BT / TT * 16;
     constexpr int WH = BE * BK / 4 / NT;               // float4 Wg loads per thread
-    static_assert(BT == 64 || BT == 32, "64- or 32-token tiles");
+    constexpr int XPT = BT * BK / NT;                  // x elements per thread per stage (8 or 4)
+    static_assert((BT == 64 || BT == 32) && (TT == 4 || TT == 2), "64- or 32-token tiles, 4 or 2 tokens per thread");
     __shared__ __attribute__((aligned(16))) float xs[2][BK][BT];
     __shared__ __attribute__((aligned(16))) float wsm[2][BK][BE + WPAD];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int e0 = blockIdx.x * BE, t0 = blockIdx.y * BT;
-    // loader roles: x -> token tid % BT, 8 consecutive i at (tid / BT) * 8; Wg -> experts tid / 8 +
+    // loader roles: x -> token tid % BT, XPT consecutive i at (tid / BT) * XPT; Wg -> experts tid / 8 +
     // (NT / 8) * h, 4 consecutive i at (tid % 8) * 4
-    const int lx_t = tid % BT, lx_k = (tid / BT) * 8;
+    const int lx_t = tid % BT, lx_k = (tid / BT) * XPT;
     const int lw_e = tid >> 3, lw_k = (tid & 7) * 4;
     const bool x_ok = t0 + lx_t < T;
     const XT* xrow = x + (size_t)min(t0 + lx_t, T - 1) * d + lx_k;
+    using XL = typename std::conditional<XPT == 8, X8<XT>, X4<XT>>::type;
     struct Regs {
-        X8<XT> x;
+        XL x;
         W4 w[WH];
     };
     auto load = [&](Regs& r, int k0) {
@@ -102,10 +129,10 @@ __global__ __launch_bounds__(BT * 4) void router_logits_many_kernel(const XT* __
         for (int h = 0; h < WH; h++) r.w[h].load(Wg, e0 + lw_e + (NT / 8) * h, k0 + lw_k, E, d);
     };
     auto store = [&](const Regs& r, int b) {
-        float v[8];
+        float v[XPT];
         r.x.get(v, x_ok);
 #pragma unroll
-        for (int j = 0; j < 8; j++) xs[b][lx_k + j][lx_t] = v[j];
+        for (int j = 0; j < XPT; j++) xs[b][lx_k + j][lx_t] = v[j];
 #pragma unroll
         for (int h = 0; h < WH; h++) {
             const int e = lw_e + (NT / 8) * h;
@@ -117,20 +144,27 @@ __global__ __launch_bounds__(BT * 4) void router_logits_many_kernel(const XT* __
         }
     };
 
-    float acc[4][4];
+    float acc[TT][4];
 #pragma unroll
-    for (int r = 0; r < 4; r++)
+    for (int r = 0; r < TT; r++)
 #pragma unroll
         for (int c = 0; c < 4; c++) acc[r][c] = 0.0f;
 
     auto compute = [&](int b) {
 #pragma unroll 8
         for (int kk = 0; kk < BK; kk++) {
-            const float4 a = *(const float4*)&xs[b][kk][ty * 4];
+            float av[TT];
+            if constexpr (TT == 4) {
+                const float4 a = *(const float4*)&xs[b][kk][ty * 4];
+                av[0] = a.x; av[1] = a.y; av[2] = a.z; av[3] = a.w;
+            } else {
+                const float2 a = *(const float2*)&xs[b][kk][ty * 2];
+                av[0] = a.x; av[1] = a.y;
+            }
             const float4 w = *(const float4*)&wsm[b][kk][tx * 4];
-            const float av[4] = {a.x, a.y, a.z, a.w}, wv[4] = {w.x, w.y, w.z, w.w};
+            const float wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int r = 0; r < 4; r++)
+            for (int r = 0; r < TT; r++)
 #pragma unroll
                 for (int c = 0; c < 4; c++) acc[r][c] = __builtin_fmaf(av[r], wv[c], acc[r][c]);
         }
@@ -155,8 +189,8 @@ __global__ __launch_bounds__(BT * 4) void router_logits_many_kernel(const XT* __
         __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int t = t0 + ty * 4 + r;
+    for (int r = 0; r < TT; r++) {
+        const int t = t0 + ty * TT + r;
         if (t >= T) continue;
 #pragma unroll
         for (int c = 0; c < 4; c++) {
@@ -283,15 +317,15 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
         // 32-token tiles: twice the blocks, so a few thousand tokens still put several blocks on a CU
         dim3 grid((E + 63) / 64, (T + 31) / 32);
         if (bf)
-            router_logits_many_kernel<uint16_t, 32><<<grid, 128, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<uint16_t, 32, 2><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_many_kernel<float, 32><<<grid, 128, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<float, 32, 2><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     } else {
         dim3 grid((E + 63) / 64, (T + 63) / 64);
         if (bf)
-            router_logits_many_kernel<uint16_t, 64><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<uint16_t, 64, 4><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_many_kernel<float, 64><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            router_logits_many_kernel<float, 64, 4><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     }
     return hipGetLastError();
 }
