@@ -10,51 +10,82 @@
 
 namespace moe {
 
-template <bool ACT_BF16>
+// K > 0: k fixed at compile time, so the slot sort is a register-only network and the k + 1 row loads of a
+// vector are all in flight together; K = 0: any k <= 16, one row load at a time.
+template <bool ACT_BF16, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ pos, const float* __restrict__ w,
-                                                      const uint8_t* __restrict__ y_rows, int T, int d, int k,
+                                                      const uint8_t* __restrict__ y_rows, int T, int d, int k_rt,
                                                       uint8_t* __restrict__ y)
 {
     constexpr int EB = ACT_BF16 ? 2 : 4;           // bytes per element
     constexpr int VE = 16 / EB;                    // elements per 16-byte vector
+    constexpr int KM = K > 0 ? K : 16;
+    const int k = K > 0 ? K : k_rt;
     const int t = blockIdx.x;
-    int rr[16];
-    float ww[16];
+    int rr[KM];
+    float ww[KM];
     for (int j = 0; j < k; j++) {
         rr[j] = pos[(size_t)t * k + j];
         ww[j] = w[(size_t)t * k + j];
     }
-    // ascending row order (insertion sort of <= 16 entries; same on every thread)
-    for (int a = 1; a < k; a++) {
-        const int r = rr[a];
-        const float v = ww[a];
-        int b = a - 1;
-        while (b >= 0 && rr[b] > r) {
-            rr[b + 1] = rr[b];
-            ww[b + 1] = ww[b];
-            b--;
+    // ascending row order (the same on every thread)
+    if constexpr (K > 0) {
+        // odd-even transposition: K rounds of compare-exchange on fixed pairs sort K entries
+#pragma unroll
+        for (int p = 0; p < K; p++)
+#pragma unroll
+            for (int b = p & 1; b + 1 < K; b += 2) {
+                const bool sw = rr[b] > rr[b + 1];
+                const int r0 = rr[b], r1 = rr[b + 1];
+                const float w0 = ww[b], w1 = ww[b + 1];
+                rr[b] = sw ? r1 : r0;
+                rr[b + 1] = sw ? r0 : r1;
+                ww[b] = sw ? w1 : w0;
+                ww[b + 1] = sw ? w0 : w1;
+            }
+    } else {
+        for (int a = 1; a < k; a++) {              // insertion sort of <= 16 entries
+            const int r = rr[a];
+            const float v = ww[a];
+            int b = a - 1;
+            while (b >= 0 && rr[b] > r) {
+                rr[b + 1] = rr[b];
+                ww[b + 1] = ww[b];
+                b--;
+            }
+            rr[b + 1] = r;
+            ww[b + 1] = v;
         }
-        rr[b + 1] = r;
-        ww[b + 1] = v;
     }
     const int64_t shared_row = (int64_t)T * k + t;
-    // block (t, column chunk): 256 threads x one 16-byte vector each
-    for (int c = (blockIdx.y * 256 + threadIdx.x) * VE; c < d; c += gridDim.y * 256 * VE) {
+    auto add_row = [&](float (&acc)[VE], const uint4 raw, float wj) {
+        const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < VE; e++) {
+            float v;
+            if constexpr (ACT_BF16) v = __uint_as_float(e & 1 ? (wv[e / 2] & 0xFFFF0000u) : (wv[e / 2] << 16));
+            else v = __uint_as_float(wv[e]);
+            acc[e] = acc[e] + v * wj;
+        }
+    };
+    // block (t, column chunk): one 16-byte vector per thread per step
+    for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * VE; c < d; c += gridDim.y * blockDim.x * VE) {
         float acc[VE];
 #pragma unroll
         for (int e = 0; e < VE; e++) acc[e] = 0.0f;
-        for (int j = 0; j < k; j++) {
-            const uint4 raw = *(const uint4*)(y_rows + ((int64_t)rr[j] * d + c) * EB);
-            const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint4 raw;
+        if constexpr (K > 0) {
+            uint4 rows[K + 1];
 #pragma unroll
-            for (int e = 0; e < VE; e++) {
-                float v;
-                if constexpr (ACT_BF16) v = __uint_as_float(e & 1 ? (wv[e / 2] & 0xFFFF0000u) : (wv[e / 2] << 16));
-                else v = __uint_as_float(wv[e]);
-                acc[e] = acc[e] + v * ww[j];
-            }
+            for (int j = 0; j < K; j++) rows[j] = *(const uint4*)(y_rows + ((int64_t)rr[j] * d + c) * EB);
+            rows[K] = *(const uint4*)(y_rows + (shared_row * d + c) * EB);
+#pragma unroll
+            for (int j = 0; j < K; j++) add_row(acc, rows[j], ww[j]);
+            raw = rows[K];
+        } else {
+            for (int j = 0; j < k; j++) add_row(acc, *(const uint4*)(y_rows + ((int64_t)rr[j] * d + c) * EB), ww[j]);
+            raw = *(const uint4*)(y_rows + (shared_row * d + c) * EB);
         }
-        const uint4 raw = *(const uint4*)(y_rows + (shared_row * d + c) * EB);
         const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
         uint32_t o[4];
         if constexpr (ACT_BF16) {
@@ -72,23 +103,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
 }
 
-// Grid: with few tokens one block per (token, 256 vectors of the row), so decode-sized T still spreads
-// over the CUs; with many tokens one block per token, which amortises the slot sort over the row.
-static dim3 combine_grid(const moe_shape_t& s)
+#ifndef MOE_COMBINE_THREADS
+#define MOE_COMBINE_THREADS 128
+#endif
+
+// Grid: with few tokens one block per (token, column chunk), so decode-sized T still spreads over the
+// CUs; with many tokens one block per token, which amortises the slot sort over the row.  128-thread
+// blocks step a 7168-wide bf16 row in seven whole 16-byte vectors per thread.
+static dim3 combine_grid(const moe_shape_t& s, int threads)
 {
     const int ve = s.act_dtype == MOE_BF16 ? 8 : 4;
-    return dim3((unsigned)s.T, s.T >= 1024 ? 1u : (unsigned)((s.d + 256 * ve - 1) / (256 * ve)));
+    const int chunk = threads * ve;
+    return dim3((unsigned)s.T, s.T >= 1024 ? 1u : (unsigned)((s.d + chunk - 1) / chunk));
+}
+
+template <bool ACT_BF16>
+static void launch_combine_t(const moe_shape_t& s, const int32_t* pos, const float* w, const Workspace& ws, void* y,
+                             hipStream_t stream)
+{
+    const dim3 grid = combine_grid(s, MOE_COMBINE_THREADS);
+    const int T = (int)s.T, d = (int)s.d, k = (int)s.k;
+    const uint8_t* rows = (const uint8_t*)ws.y_rows;
+    uint8_t* out = (uint8_t*)y;
+    switch (k) {
+    case 4: combine_kernel<ACT_BF16, 4><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 6: combine_kernel<ACT_BF16, 6><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 8: combine_kernel<ACT_BF16, 8><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    default: combine_kernel<ACT_BF16, 0><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    }
 }
 
 hipError_t launch_combine(const moe_shape_t& s, const int32_t* pos, const float* w, const Workspace& ws, void* y,
                           hipStream_t stream)
 {
-    if (s.act_dtype == MOE_BF16)
-        combine_kernel<true><<<combine_grid(s), 256, 0, stream>>>(pos, w, (const uint8_t*)ws.y_rows, (int)s.T, (int)s.d,
-                                                                (int)s.k, (uint8_t*)y);
-    else
-        combine_kernel<false><<<combine_grid(s), 256, 0, stream>>>(pos, w, (const uint8_t*)ws.y_rows, (int)s.T, (int)s.d,
-                                                                 (int)s.k, (uint8_t*)y);
+    if (s.act_dtype == MOE_BF16) launch_combine_t<true>(s, pos, w, ws, y, stream);
+    else launch_combine_t<false>(s, pos, w, ws, y, stream);
     return hipGetLastError();
 }
 
@@ -166,10 +215,10 @@ hipError_t launch_combine_partial(const moe_shape_t& s, const int32_t* idx, cons
                                   hipStream_t stream)
 {
     if (s.act_dtype == MOE_BF16)
-        combine_partial_kernel<true><<<combine_grid(s), 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
+        combine_partial_kernel<true><<<combine_grid(s, 256), 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
                                                                         (int)s.d, (int)s.k, e0, e1, with_shared, y_partial);
     else
-        combine_partial_kernel<false><<<combine_grid(s), 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
+        combine_partial_kernel<false><<<combine_grid(s, 256), 256, 0, stream>>>(idx, pos, w, (const uint8_t*)ws.y_rows, (int)s.T,
                                                                          (int)s.d, (int)s.k, e0, e1, with_shared, y_partial);
     return hipGetLastError();
 }

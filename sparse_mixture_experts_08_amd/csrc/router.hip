@@ -203,6 +203,122 @@ __global__ __launch_bounds__(BT / TT * 16) void router_logits_many_kernel(const 
     }
 }
 
+// Seven more chains per lane for the price of one operand read: acc[j] (j = 1..7) += w' * x, where w'
+// is the first source taken from lane (l - j) mod 16 of the same 16-lane row (DPP row rotation inside
+// v_fmac_f32, which the compiler does not fold from a separate DPP move), for the four K steps of w and
+// x in order.  The leading s_nop gives the two wait states a DPP read needs after a VALU write of its
+// source.
+#define MOE_DPP_FMA(D, J, W, X) "v_fmac_f32_dpp %" #D ", %" #W ", %" #X " row_ror:" #J " row_mask:0xf bank_mask:0xf\n"
+#define MOE_DPP_FMA7(W, X)                                                                                      \
+    MOE_DPP_FMA(0, 1, W, X) MOE_DPP_FMA(1, 2, W, X) MOE_DPP_FMA(2, 3, W, X) MOE_DPP_FMA(3, 4, W, X)             \
+    MOE_DPP_FMA(4, 5, W, X) MOE_DPP_FMA(5, 6, W, X) MOE_DPP_FMA(6, 7, W, X)
+__device__ __forceinline__ void fma_rotated8(float (&a)[8], float4 w, float4 x)
+{
+    a[0] = __builtin_fmaf(x.x, w.x, a[0]);
+    a[0] = __builtin_fmaf(x.y, w.y, a[0]);
+    a[0] = __builtin_fmaf(x.z, w.z, a[0]);
+    a[0] = __builtin_fmaf(x.w, w.w, a[0]);
+    asm("s_nop 1\n" MOE_DPP_FMA7(7, 11) MOE_DPP_FMA7(8, 12) MOE_DPP_FMA7(9, 13) MOE_DPP_FMA7(10, 14)
+        : "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+        : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+#undef MOE_DPP_FMA7
+#undef MOE_DPP_FMA
+
+#ifndef MOE_DPP_BK
+#define MOE_DPP_BK 64
+#endif
+
+// Mid-sized T: per 16-lane row an outer product of 16 tokens x 8 experts with one LDS read per operand
+// per lane and K step.  Lane l reads x of token l and the gate row of expert l % 8 and, through
+// fma_rotated8, keeps eight chains: token l with the experts of lanes (l - j) mod 16, j = 0..7, which are
+// the eight experts of the row.  (The register tiles of router_logits_many_kernel read six floats per
+// eight FMAs, more than the LDS delivers at two wavefronts per SIMD.)  Block = 4 wavefronts = 64 tokens
+// x 32 experts: wavefront w takes tokens 16 w .. 16 w + 15, its four rows the four 8-expert groups.  K is
+// staged 64 at a time through double-buffered LDS as [t][i] and [e][i] rows, so a lane reads four
+// consecutive i of each operand with one 16-byte read; global loads run two stages ahead.  Every chain
+// runs over i in order.  (Prefill router, T = 4096: 0.345 ms with the register tiles, 0.31 ms here.  The
+// DPP forms issue somewhat slower than plain FMAs, so where there are enough wavefronts for the 4 x 4
+// register tiles -- T above 8192 -- those stay faster.)
+template <typename XT>
+__global__ __launch_bounds__(256) void router_logits_dpp_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
+                                                               const float* __restrict__ bias, float* __restrict__ L,
+                                                               int T, int d, int E)
+{
+    constexpr int BT = 64, BE = 32, BK = MOE_DPP_BK, PAD = 4, NQ = BK / 32;
+    static_assert(BK % 32 == 0, "whole 32-wide loader steps");
+    __shared__ __attribute__((aligned(16))) float xs[2][BT][BK + PAD];
+    __shared__ __attribute__((aligned(16))) float ws[2][BE][BK + PAD];
+    const int tid = threadIdx.x, lane = tid & 63, l = lane & 15, row = lane >> 4, wave = tid >> 6;
+    const int e0 = blockIdx.x * BE, t0 = blockIdx.y * BT;
+    // loaders, per 32 i of the stage: x -> token tid / 4, 8 consecutive i at (tid % 4) * 8; Wg -> expert
+    // tid / 8, 4 consecutive i at (tid % 8) * 4
+    const int lx_t = tid >> 2, lx_k = (tid & 3) * 8;
+    const int lw_e = tid >> 3, lw_k = (tid & 7) * 4;
+    const bool x_ok = t0 + lx_t < T;
+    const XT* xrow = x + (size_t)min(t0 + lx_t, T - 1) * d + lx_k;
+    struct Regs {
+        X8<XT> x[NQ];
+        W4 w[NQ];
+    };
+    auto load = [&](Regs& r, int k0) {
+#pragma unroll
+        for (int q = 0; q < NQ; q++) {
+            r.x[q].load(xrow + k0 + 32 * q);
+            r.w[q].load(Wg, e0 + lw_e, k0 + 32 * q + lw_k, E, d);
+        }
+    };
+    auto store = [&](const Regs& r, int b) {
+#pragma unroll
+        for (int q = 0; q < NQ; q++) {
+            float v[8];
+            r.x[q].get(v, x_ok);
+            *(float4*)&xs[b][lx_t][32 * q + lx_k] = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)&xs[b][lx_t][32 * q + lx_k + 4] = make_float4(v[4], v[5], v[6], v[7]);
+            *(float4*)&ws[b][lw_e][32 * q + lw_k] = r.w[q].get(e0 + lw_e < E);
+        }
+    };
+
+    const int my_t = wave * 16 + l, my_e = row * 8 + (l & 7);
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[j] = 0.0f;
+    auto compute = [&](int b) {
+#pragma unroll
+        for (int kq = 0; kq < BK; kq += 4)
+            fma_rotated8(acc, *(const float4*)&ws[b][my_e][kq], *(const float4*)&xs[b][my_t][kq]);
+    };
+    const int ns = d / BK;
+    Regs ra, rb;
+    load(ra, 0);
+    if (ns > 1) load(rb, BK);
+    store(ra, 0);
+    __syncthreads();
+    for (int s = 0; s < ns; s += 2) {
+        // stage s is in LDS buffer 0; rb holds stage s + 1 (in flight)
+        if (s + 2 < ns) load(ra, (s + 2) * BK);
+        compute(0);
+        if (s + 1 >= ns) break;
+        store(rb, 1);
+        __syncthreads();
+        // stage s + 1 is in LDS buffer 1; ra holds stage s + 2 (in flight)
+        if (s + 3 < ns) load(rb, (s + 3) * BK);
+        compute(1);
+        if (s + 2 < ns) store(ra, 0);
+        __syncthreads();
+    }
+    const int t = t0 + my_t;
+    if (t >= T) return;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int e = e0 + row * 8 + ((l - j) & 7);        // row_ror:j read lane (l - j) mod 16
+        if (e >= E) continue;
+        float v = acc[j];
+        if (bias) v = v + bias[e];
+        L[(size_t)t * E + e] = v;
+    }
+}
+
 // Few tokens: one chain per lane.  Block = TPB tokens x 16 experts, TPB / 4 wavefronts (lane (tt, el)
 // = (thread / 16, thread % 16)).  Per 128-wide K stage the block copies the Wg tile (16 gate rows, 512
 // bytes each) and the x tile (TPB token rows) into LDS as [e][i] and [t][i], so each lane reads four
@@ -291,6 +407,9 @@ __global__ __launch_bounds__(TPB * 16) void router_logits_few_kernel(const XT* _
 #ifndef MOE_ROUTER_FEW_MAX_T
 #define MOE_ROUTER_FEW_MAX_T 512
 #endif
+#ifndef MOE_ROUTER_DPP
+#define MOE_ROUTER_DPP 1
+#endif
 #ifndef MOE_ROUTER_BT32_MAX_T
 #define MOE_ROUTER_BT32_MAX_T 8192
 #endif
@@ -314,6 +433,14 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
         else
             router_logits_few_kernel<float, 16><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     } else if (T <= MOE_ROUTER_BT32_MAX_T) {
+#if MOE_ROUTER_DPP
+        dim3 grid_r((E + 31) / 32, (T + 63) / 64);
+        if (bf)
+            router_logits_dpp_kernel<uint16_t><<<grid_r, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+        else
+            router_logits_dpp_kernel<float><<<grid_r, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+        return hipGetLastError();
+#endif
         // 32-token tiles: twice the blocks, so a few thousand tokens still put several blocks on a CU
         dim3 grid((E + 63) / 64, (T + 31) / 32);
         if (bf)
