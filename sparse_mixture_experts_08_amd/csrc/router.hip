@@ -319,82 +319,107 @@ __global__ __launch_bounds__(256) void router_logits_dpp_kernel(const XT* __rest
     }
 }
 
+
 // Few tokens: one chain per lane.  Block = TPB tokens x 16 experts, TPB / 4 wavefronts (lane (tt, el)
-// = (thread / 16, thread % 16)).  Per 128-wide K stage the block copies the Wg tile (16 gate rows, 512
-// bytes each) and the x tile (TPB token rows) into LDS as [e][i] and [t][i], so each lane reads four
-// consecutive i of its expert and of its token with one 16-byte read.  Global loads run two stages
-// ahead of the FMAs (two register sets, loop unrolled by two).
-template <typename XT, int TPB>
+// = (thread / 16, thread % 16)).  Per BK-wide K stage the block copies the Wg tile (16 gate rows) and the
+// x tile (TPB token rows) into LDS as [e][i] and [t][i], so each lane reads four consecutive i of its
+// expert and of its token with one 16-byte read.  Global loads run two stages ahead of the FMAs (two
+// register sets, loop unrolled by two) and are issued without a branch around them (past the end the
+// last stage is loaded again): behind a branch the compiler waits for every load in flight before
+// issuing the next set.  With one chain per lane a stage is short next to the load latency, so the
+// stages are wide (BK = 256 where d allows; decode router, T = 64: 50 us with 128-wide stages and no LDS
+// prefetch, 40 us here).
+template <typename XT, int TPB, int BK>
 __global__ __launch_bounds__(TPB * 16) void router_logits_few_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
                                                                      const float* __restrict__ bias, float* __restrict__ L,
                                                                      int T, int d, int E)
 {
-    constexpr int BK = 128, PAD = 4, NT = TPB * 16;
-    constexpr int WPT = 16 * 16 / NT;                          // 8-float Wg chunks per thread
+    constexpr int PAD = 4, NT = TPB * 16, Q = BK / 128;
+    constexpr int WPT = 16 * 16 / NT;                          // 8-float Wg chunks per thread per 128 i
     static_assert(TPB % 4 == 0 && TPB <= 16, "whole wavefronts, at most 16 tokens");
+    static_assert(BK % 128 == 0, "whole 128-wide loader steps");
     __shared__ __attribute__((aligned(16))) float wT[2][16][BK + PAD];
     __shared__ __attribute__((aligned(16))) float xT[2][TPB][BK + PAD];
     const int tid = threadIdx.x, tt = tid >> 4, el = tid & 15;
     const int e0 = blockIdx.x * 16, t0 = blockIdx.y * TPB;
-    const int li = (tid & 15) * 8;                             // first i of this thread's chunks
+    const int li = (tid & 15) * 8;                             // first i of this thread's chunks, per 128
     const bool x_ok = t0 + tt < T;
     const XT* xrow = x + (size_t)min(t0 + tt, T - 1) * d + li;
 
     struct Regs {
-        W4 w[WPT][2];
-        X8<XT> x;
+        W4 w[Q][WPT][2];
+        X8<XT> x[Q];
     };
     auto load = [&](Regs& r, int k0) {
 #pragma unroll
-        for (int p = 0; p < WPT; p++) {
-            const int e = (tid >> 4) + p * TPB;
-            r.w[p][0].load(Wg, e0 + e, k0 + li, E, d);
-            r.w[p][1].load(Wg, e0 + e, k0 + li + 4, E, d);
+        for (int q = 0; q < Q; q++) {
+#pragma unroll
+            for (int p = 0; p < WPT; p++) {
+                const int e = (tid >> 4) + p * TPB;
+                r.w[q][p][0].load(Wg, e0 + e, k0 + 128 * q + li, E, d);
+                r.w[q][p][1].load(Wg, e0 + e, k0 + 128 * q + li + 4, E, d);
+            }
+            r.x[q].load(xrow + k0 + 128 * q);
         }
-        r.x.load(xrow + k0);
     };
     auto store = [&](const Regs& r, int b) {
 #pragma unroll
-        for (int p = 0; p < WPT; p++) {
-            const int e = (tid >> 4) + p * TPB;
-            *(float4*)&wT[b][e][li] = r.w[p][0].get(e0 + e < E);
-            *(float4*)&wT[b][e][li + 4] = r.w[p][1].get(e0 + e < E);
+        for (int q = 0; q < Q; q++) {
+#pragma unroll
+            for (int p = 0; p < WPT; p++) {
+                const int e = (tid >> 4) + p * TPB;
+                *(float4*)&wT[b][e][128 * q + li] = r.w[q][p][0].get(e0 + e < E);
+                *(float4*)&wT[b][e][128 * q + li + 4] = r.w[q][p][1].get(e0 + e < E);
+            }
+            float v[8];
+            r.x[q].get(v, x_ok);
+            *(float4*)&xT[b][tt][128 * q + li] = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)&xT[b][tt][128 * q + li + 4] = make_float4(v[4], v[5], v[6], v[7]);
         }
-        float v[8];
-        r.x.get(v, x_ok);
-        *(float4*)&xT[b][tt][li] = make_float4(v[0], v[1], v[2], v[3]);
-        *(float4*)&xT[b][tt][li + 4] = make_float4(v[4], v[5], v[6], v[7]);
     };
     float acc = 0.0f;
+    // The stage's LDS reads run D steps of four i ahead of the single FMA chain (pinned there by the
+    // scheduling barriers): with one wavefront per SIMD nothing else hides their latency.
     auto compute = [&](int b) {
-#pragma unroll 8
-        for (int i = 0; i < BK; i += 4) {
-            const float4 a = *(const float4*)&xT[b][tt][i];
-            const float4 w = *(const float4*)&wT[b][el][i];
-            acc = __builtin_fmaf(a.x, w.x, acc);
-            acc = __builtin_fmaf(a.y, w.y, acc);
-            acc = __builtin_fmaf(a.z, w.z, acc);
-            acc = __builtin_fmaf(a.w, w.w, acc);
+        constexpr int N = BK / 4, D = 16;
+        float4 fa[N], fw[N];
+#pragma unroll
+        for (int j = 0; j < D; j++) {
+            fa[j] = *(const float4*)&xT[b][tt][4 * j];
+            fw[j] = *(const float4*)&wT[b][el][4 * j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            if (i + D < N) {
+                fa[i + D] = *(const float4*)&xT[b][tt][4 * (i + D)];
+                fw[i + D] = *(const float4*)&wT[b][el][4 * (i + D)];
+            }
+            acc = __builtin_fmaf(fa[i].x, fw[i].x, acc);
+            acc = __builtin_fmaf(fa[i].y, fw[i].y, acc);
+            acc = __builtin_fmaf(fa[i].z, fw[i].z, acc);
+            acc = __builtin_fmaf(fa[i].w, fw[i].w, acc);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     const int ns = d / BK;
     Regs ra, rb;
     load(ra, 0);
-    if (ns > 1) load(rb, BK);
+    load(rb, min(1, ns - 1) * BK);
     store(ra, 0);
     __syncthreads();
     for (int s = 0; s < ns; s += 2) {
         // stage s is in LDS buffer 0; rb holds stage s + 1 (in flight)
-        if (s + 2 < ns) load(ra, (s + 2) * BK);
+        load(ra, min(s + 2, ns - 1) * BK);
         compute(0);
         if (s + 1 >= ns) break;
         store(rb, 1);
         __syncthreads();
         // stage s + 1 is in LDS buffer 1; ra holds stage s + 2 (in flight)
-        if (s + 3 < ns) load(rb, (s + 3) * BK);
+        load(rb, min(s + 3, ns - 1) * BK);
         compute(1);
-        if (s + 2 < ns) store(ra, 0);
+        store(ra, 0);
         __syncthreads();
     }
     const int t = t0 + tt, e = e0 + el;
@@ -402,6 +427,18 @@ __global__ __launch_bounds__(TPB * 16) void router_logits_few_kernel(const XT* _
         if (bias) acc = acc + bias[e];
         L[(size_t)t * E + e] = acc;
     }
+}
+
+
+// The few-token kernel with 256-wide K stages where d allows (512-wide ones measured slower), else 128.
+template <typename XT, int TPB>
+static void launch_few(dim3 grid, const XT* x, const float* Wg, const float* bias, float* logits, int T, int d, int E,
+                       hipStream_t stream)
+{
+    if (d % 256 == 0)
+        router_logits_few_kernel<XT, TPB, 256><<<grid, TPB * 16, 0, stream>>>(x, Wg, bias, logits, T, d, E);
+    else
+        router_logits_few_kernel<XT, TPB, 128><<<grid, TPB * 16, 0, stream>>>(x, Wg, bias, logits, T, d, E);
 }
 
 #ifndef MOE_ROUTER_FEW_MAX_T
@@ -422,16 +459,12 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
     if (T <= 256) {
         // 8 tokens per block: twice the blocks of the 16-token form, more loads in flight per token
         dim3 grid((E + 15) / 16, (T + 7) / 8);
-        if (bf)
-            router_logits_few_kernel<uint16_t, 8><<<grid, 128, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
-        else
-            router_logits_few_kernel<float, 8><<<grid, 128, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+        if (bf) launch_few<uint16_t, 8>(grid, (const uint16_t*)x, Wg, bias, logits, T, d, E, stream);
+        else launch_few<float, 8>(grid, (const float*)x, Wg, bias, logits, T, d, E, stream);
     } else if (T <= MOE_ROUTER_FEW_MAX_T) {
         dim3 grid((E + 15) / 16, (T + 15) / 16);
-        if (bf)
-            router_logits_few_kernel<uint16_t, 16><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
-        else
-            router_logits_few_kernel<float, 16><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+        if (bf) launch_few<uint16_t, 16>(grid, (const uint16_t*)x, Wg, bias, logits, T, d, E, stream);
+        else launch_few<float, 16>(grid, (const float*)x, Wg, bias, logits, T, d, E, stream);
     } else if (T <= MOE_ROUTER_BT32_MAX_T) {
 #if MOE_ROUTER_DPP
         dim3 grid_r((E + 31) / 32, (T + 63) / 64);
