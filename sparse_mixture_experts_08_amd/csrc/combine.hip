@@ -68,24 +68,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
             acc[e] = acc[e] + v * wj;
         }
     };
-    // block (t, column chunk): one 16-byte vector per thread per step
-    for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * VE; c < d; c += gridDim.y * blockDim.x * VE) {
-        float acc[VE];
-#pragma unroll
-        for (int e = 0; e < VE; e++) acc[e] = 0.0f;
-        uint4 raw;
-        if constexpr (K > 0) {
-            uint4 rows[K + 1];
-#pragma unroll
-            for (int j = 0; j < K; j++) rows[j] = *(const uint4*)(y_rows + ((int64_t)rr[j] * d + c) * EB);
-            rows[K] = *(const uint4*)(y_rows + (shared_row * d + c) * EB);
-#pragma unroll
-            for (int j = 0; j < K; j++) add_row(acc, rows[j], ww[j]);
-            raw = rows[K];
-        } else {
-            for (int j = 0; j < k; j++) add_row(acc, *(const uint4*)(y_rows + ((int64_t)rr[j] * d + c) * EB), ww[j]);
-            raw = *(const uint4*)(y_rows + (shared_row * d + c) * EB);
-        }
+    auto finish = [&](const float (&acc)[VE], const uint4 raw, int c) {
         const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
         uint32_t o[4];
         if constexpr (ACT_BF16) {
@@ -100,6 +83,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
             for (int e = 0; e < 4; e++) o[e] = __float_as_uint(acc[e] + __uint_as_float(wv[e]));
         }
         *(uint4*)(y + ((int64_t)t * d + c) * EB) = make_uint4(o[0], o[1], o[2], o[3]);
+    };
+    const int step = gridDim.y * blockDim.x * VE;
+    int c = (blockIdx.y * blockDim.x + threadIdx.x) * VE;
+    if constexpr (K > 0) {
+        // The k + 1 rows of the next vector are loaded while this one is summed (past the row end the
+        // current vector again, with no branch around the loads).
+        auto load = [&](uint4 (&rows)[K + 1], int cc) {
+#pragma unroll
+            for (int j = 0; j < K; j++) rows[j] = *(const uint4*)(y_rows + ((int64_t)rr[j] * d + cc) * EB);
+            rows[K] = *(const uint4*)(y_rows + (shared_row * d + cc) * EB);
+        };
+        if (c >= d) return;
+        uint4 cur[K + 1];
+        load(cur, c);
+        for (; c < d; c += step) {
+            uint4 nxt[K + 1];
+            load(nxt, c + step < d ? c + step : c);
+            float acc[VE];
+#pragma unroll
+            for (int e = 0; e < VE; e++) acc[e] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < K; j++) add_row(acc, cur[j], ww[j]);
+            finish(acc, cur[K], c);
+#pragma unroll
+            for (int j = 0; j <= K; j++) cur[j] = nxt[j];
+        }
+    } else {
+        for (; c < d; c += step) {
+            float acc[VE];
+#pragma unroll
+            for (int e = 0; e < VE; e++) acc[e] = 0.0f;
+            for (int j = 0; j < k; j++) add_row(acc, *(const uint4*)(y_rows + ((int64_t)rr[j] * d + c) * EB), ww[j]);
+            finish(acc, *(const uint4*)(y_rows + (shared_row * d + c) * EB), c);
+        }
     }
 }
 
