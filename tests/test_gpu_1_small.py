@@ -52,6 +52,26 @@ def test_edge_shapes(wl):
     run_parity(wl, inp)
 
 
+@pytest.mark.parametrize("T,E,act", [
+    (256, 64, BF16), (257, 64, BF16),      # few-token router: 8- then 16-token blocks
+    (512, 40, F32), (513, 40, F32),        # ... then the DPP row-rotation kernel (E not a multiple of 32)
+    (513, 64, BF16), (2500, 257, BF16),    # ragged 64-token and 32-expert tails
+    (8192, 64, BF16), (8193, 72, BF16),    # DPP kernel's last size, then the 64 x 64 register tiles
+], ids=lambda v: str(v))
+def test_router_kernel_boundaries(T, E, act):
+    # Routing of every token, bit for bit against the oracle, on both sides of each router kernel switch,
+    # with a bias (one fp32 add after the chain).
+    from gpu_util import check_routing
+    wl = W.Workload("router-edge", T, 512, E, 4, 128, 128, act, act)
+    inp = W.generate(wl, seed=11, device=DEV, weights=False)
+    g = torch.Generator().manual_seed(T)
+    inp["bias"] = (torch.randn(E, generator=g) * 0.01).to(DEV)
+    say(f"[router-edge] T={T} E={E} act={act}")
+    r = B.moe_route(inp["x"], inp["Wg"], inp["bias"], wl.k)
+    torch.cuda.synchronize()
+    check_routing(wl, r, oracle_route(wl, host(inp)))
+
+
 def test_all_tokens_to_one_expert_and_zero_count_experts():
     # +1e4 logit bias on one expert: it receives every token (one long group), all others but k-1 get
     # few or none.
