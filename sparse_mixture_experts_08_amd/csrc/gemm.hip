@@ -1068,6 +1068,9 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 #ifndef MOE_KROT_UP
 #define MOE_KROT_UP 3
 #endif
+#ifndef MOE_KROT_WDN
+#define MOE_KROT_WDN 3      // wide-kernel down GEMM (rotations 0 / 1 / 5 / 7 / 13 measured slower)
+#endif
 #ifndef MOE_KROT_DN
 #define MOE_KROT_DN 1
 #endif
@@ -1083,7 +1086,6 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 template <bool UP>
 static void launch_w(GemmArgs a, hipStream_t stream)
 {
-    a.krot = MOE_KROT_UP;
     const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
     grouped_gemm_w_kernel<UP, 256, 128, 2, 8><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
@@ -1233,6 +1235,7 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
         launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
     } else if (wide) {
         dn.n_blocks = (int)(s.d / 256);
+        dn.krot = MOE_KROT_WDN;
         launch_w<false>(dn, stream);
     } else {
         dn.n_blocks = (int)(s.d / 128);
