@@ -15,7 +15,6 @@ around it on the launch stream, over the timed steps) and the CPU oracle timed o
 """
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -28,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from sparse_mixture_experts_08_amd import binding as B  # noqa: E402
+from sparse_mixture_experts_08_amd.build import code_fingerprint  # noqa: E402
 from sparse_mixture_experts_08_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
@@ -94,14 +94,14 @@ def algorithmic(wl, counts, e0=0, e1=None, n_shared=None):
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it
-    was taken on the current GEMM source (else None)."""
+    was taken on the current GEMM code (its comment-free fingerprint; else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))[workload]
     except (OSError, KeyError, ValueError):
         return None
     src = os.path.join(ROOT, "sparse_mixture_experts_08_amd", "csrc", "gemm.hip")
-    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec.get("gemm_source_sha256_16"):
+    if code_fingerprint(src) != rec.get("gemm_code_sha256_16"):
         return None
     k = rec.get(kernel)
     return None if not k else k["bytes"]

@@ -6,17 +6,19 @@ TRACE_DIR holds the CSV output of `rocprofv3 --kernel-trace --stats -f csv -o ru
 that of `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` over a bench.py run that ends with one plain
 1 GiB device copy (`--copy-calibration-mib 1024`).  Writes profiles/kernels_<workload>[_<variant>].md
 (kernel durations and HBM bytes per dispatch) and records the grouped GEMMs' bytes per launch, scaled by
-what the counters read for the known-size copy, in profiles/traffic.json under the hash of the GEMM
-source they were taken on (bench.py reports them only while that hash matches).
+what the counters read for the known-size copy, in profiles/traffic.json under the fingerprint of the GEMM
+code they were taken on (sha256[:16] of csrc/gemm.hip without comments or whitespace; bench.py reports
+them only while it matches).
 """
 import csv
 import glob
-import hashlib
 import json
 import os
 import re
 import sys
 from collections import defaultdict
+
+from sparse_mixture_experts_08_amd.build import code_fingerprint
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_08_amd", "csrc", "gemm.hip")
@@ -87,7 +89,7 @@ def main():
               f"WRITE x{wf:.3f}.", "",
               "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB (scaled) | written GB (scaled) |",
               "|---|---|---|---|---|---|"]
-    rec = {"gemm_source_sha256_16": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16],
+    rec = {"gemm_code_sha256_16": code_fingerprint(GEMM_SRC),
            "fetch_factor": ff, "write_factor": wf}
     for k in sorted(fetch):
         if "moe::" not in k:
@@ -99,7 +101,8 @@ def main():
         role = gemm_role(k)
         if role:
             rec[role] = {"kernel": k, "bytes": (rb + wb) * 1e9}
-    lines += ["", f"Kernel source hash (sha256[:16] of csrc/gemm.hip) when measured: `{rec['gemm_source_sha256_16']}`",
+    lines += ["", "GEMM code fingerprint when measured (sha256[:16] of csrc/gemm.hip without comments or whitespace): "
+              f"`{rec['gemm_code_sha256_16']}`",
               ""]
     name = f"kernels_{workload}" + ("" if variant == "layer" else f"_{variant}") + ".md"
     open(os.path.join(ROOT, "profiles", name), "w").write("\n".join(lines))

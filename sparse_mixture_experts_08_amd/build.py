@@ -1,5 +1,7 @@
 """Build libmoe.so (the HIP kernels and the C ABI of include/moe.h) in-tree for gfx950 with hipcc."""
+import hashlib
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -15,6 +17,17 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 vector ops are switched off for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")]
+
+
+_TOKEN = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_fingerprint(path: str) -> str:
+    """sha256[:16] of a C++/HIP source with its comments removed and whitespace collapsed: it changes with
+    the code, not with a comment or layout edit (measurements stored against it stay valid across those)."""
+    text = open(path).read()
+    code = _TOKEN.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()[:16]
 
 
 def _compile(src: str, verbose: bool) -> str:

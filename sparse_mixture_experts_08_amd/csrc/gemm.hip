@@ -559,8 +559,11 @@ __device__ __forceinline__ void store_tile_bf16(const uint8_t* tile, uint8_t* ou
 // the barrier publishing the next stage, the refill of the freed buffer and the first fragment reads of
 // the next stage sit under the MFMAs of the stage's last K step.  With whole-line (128-byte) rows the
 // time of this kernel on MI355X is set mostly by the global -> LDS copies (the same loop without MFMAs
-// takes about 80 % of it, without the copies about 60 %): the per-CU rate of L2 line requests, hit or
-// miss, not HBM bandwidth, which is why the block tile is as large as the register file allows.
+// takes 77-94 % of it, without the copies about 60 %).  The copy path itself is not the cap: the same
+// direct-to-LDS loads alone stream 58-61 B/clock per CU from L2 and the same panel pattern 6.1 TB/s from
+// HBM; deeper rings, copies issued ahead of the barrier, other XCD groupings and K rotations did not
+// shorten it.  Fewer staged bytes per MFMA did, which is why the block tile is as large as the register
+// file allows.
 // ---------------------------------------------------------------------------------------------------
 template <bool UP, int BM, int RB, int NSTG, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
