@@ -66,17 +66,17 @@ def main():
     stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
     moe = [r for r in stats if "moe::" in r["Name"]]
     lines = [f"# rocprofv3 kernel summary: {key}", "",
-             "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; R = repository root):", "", "```"]
+             "Commands (run from /tmp with TMPDIR=/tmp on an MI355X; R = repository root, OUT = an output "
+             "directory):", "", "```"]
     v = f" --variant {variant}"
     bench = f"python3 $R/bench.py --workload {workload}{v}"
-    lines.append(f"rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o run -- {bench} "
+    lines.append(f"rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace -o run -- {bench} "
                  "--steps 10 --warmup 2 --no-cpu-baseline")
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         lines.append(f'rocprofv3 --pmc {c} --kernel-include-regex "moe::|copyBuffer" -f csv -d '
-                     f"$R/gpurun_out/prof_{c} -o run -- {bench} --steps 1 --warmup 1 --no-cpu-baseline "
+                     f"$OUT/{c} -o run -- {bench} --steps 1 --warmup 1 --no-cpu-baseline "
                      "--copy-calibration-mib 1024")
-    lines.append(f"python3 $R/rocprof_summary.py {workload} {variant} $R/gpurun_out/prof_trace "
-                 "$R/gpurun_out/prof_FETCH_SIZE $R/gpurun_out/prof_WRITE_SIZE")
+    lines.append(f"python3 $R/rocprof_summary.py {workload} {variant} $OUT/trace $OUT/FETCH_SIZE $OUT/WRITE_SIZE")
     lines += ["```", "", "## Kernel durations (--kernel-trace --stats; every dispatch in the run, including the "
               "staged pass)", "", "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in moe:
