@@ -1,0 +1,44 @@
+"""bench.py on the GPU: one run of the small fp32 workload prints one JSON line with every field of the
+benchmark contract, a roofline for the dominant kernel and the CPU oracle baseline."""
+import contextlib
+import io
+import json
+import os
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line():
+    sys.path.insert(0, ROOT)
+    import bench
+    argv = sys.argv
+    sys.argv = ["bench.py", "--workload", "tiny-fp32-T128-d512-E32-k4", "--steps", "3", "--warmup", "1",
+                "--cpu-tokens", "8"]
+    buf = io.StringIO()
+    try:
+        with contextlib.redirect_stdout(buf):
+            bench.main()
+    finally:
+        sys.argv = argv
+    lines = [l for l in buf.getvalue().splitlines() if l.strip()]
+    assert len(lines) == 1, lines
+    r = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in r, key
+    assert r["n_gpus"] == 1 and r["steps"] == 3 and r["warmup"] == 1
+    assert r["value"] > 0 and r["ms_per_step"] > 0
+    assert r["config"]["workload"] == "tiny-fp32-T128-d512-E32-k4"
+    roof = r["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    assert roof["bound"] in ("hbm", "mfma", "alu") and roof["peak"] > 0 and roof["achieved"] > 0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) <= 1e-6 * max(1.0, roof["frac"])
+    cb = r["cpu_baseline"]
+    for key in ("value", "unit", "cores", "kind", "sample"):
+        assert key in cb, key
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
