@@ -177,3 +177,36 @@ def test_concurrent_calls_on_two_streams():
     for ya, yb in outs:
         assert torch.equal(ya.view(torch.int16), ya_ref.view(torch.int16))
         assert torch.equal(yb.view(torch.int16), yb_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("wl", [
+    W.Workload("graph-decode", 64, 512, 64, 8, 256, 256, BF16, BF16),     # fused routing, 16-row tiles
+    W.Workload("graph-prefill", 900, 512, 16, 4, 256, 384, BF16, BF16),   # multi-kernel routing, 256-row tiles
+    W.Workload("graph-fp8", 500, 512, 16, 4, 256, 256, BF16, FP8),
+], ids=lambda w: w.name)
+def test_hip_graph_capture_and_replay(wl):
+    # The forward pass enqueues no memset, allocation or host synchronisation, so it records into a HIP graph
+    # as is.  Every replay -- with eager calls of the same layer between them -- matches the eager output
+    # bit for bit.
+    inp = W.generate(wl, seed=14, device=DEV)
+    shape = B.make_shape(wl.T, wl.d, wl.E, wl.k, wl.inter, wl.inter_shared, wl.act_dtype, wl.w_dtype)
+    ws = torch.empty(B.moe_workspace_size(shape), dtype=torch.uint8, device=DEV)
+    y = torch.empty_like(inp["x"])
+    y_ref = B.forward_inputs(inp, wl.k)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.forward_inputs(inp, wl.k, y=y, workspace=ws)          # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.forward_inputs(inp, wl.k, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+        y_eager = B.forward_inputs(inp, wl.k)
+        torch.cuda.synchronize()
+        assert torch.equal(y_eager.view(torch.int16), y_ref.view(torch.int16))
