@@ -90,7 +90,7 @@ struct Workspace {
     int32_t* pos;           // [T * k]
     int32_t* row_token;     // [T * k + T]  token of each expert-sorted row; shared rows last
     int4* tiles;            // [max_tiles]  (group, first row, rows, 0); group E is the shared expert
-    int32_t* sync;          // [4]  tile count, completion ticket
+    int32_t* sync;          // [4]  sync[0]: number of tiles (written with the tile list)
     uint8_t* xq;            // [T, d] E4M3 codes of x (fp8 weights only)
     float* xs;              // [T, d / 128] their scales
     void* h;                // [T * k + T, inter_max] act dtype, or E4M3 codes (fp8 weights)

@@ -11,8 +11,8 @@
 // Sorted rows [0, T*k) hold the routed slots; rows [T*k, T*k + T) are the shared expert's, token order.
 //
 // Two paths: up to 256 tokens, one block does top-k, masks, scans, scatter and tiles in one launch;
-// beyond that, a top-k kernel per chunk (router.hip), a per-expert scan whose last block writes offsets
-// and tiles, and a scatter kernel.
+// beyond that, a top-k kernel per chunk (router.hip), a per-expert scan over the chunks, and a scatter
+// kernel whose every block scans the expert counts itself (block 0 also stores offsets and the tiles).
 #include "moe_common.h"
 #include "topk.h"
 
@@ -138,14 +138,11 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restri
 // ---------------------------------------------------------------------------------------------------
 // Multi-block path.
 // ---------------------------------------------------------------------------------------------------
+// One block per expert: the exclusive scan of its per-chunk counts over the chunks, and its total.
 __global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int E,
-                                                         int T, int k, int bm, TileRange tr, int32_t* __restrict__ chunk_prefix,
-                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                         int4* __restrict__ tiles, int32_t* __restrict__ sync)
+                                                         int32_t* __restrict__ chunk_prefix, int32_t* __restrict__ counts)
 {
     __shared__ int scan_lds[5];
-    __shared__ int cnt[1024], off[1025];
-    __shared__ int is_last;
     const int e = blockIdx.x, tid = threadIdx.x;
     const int per = (nchunks + 255) / 256;
     const int c0 = tid * per, c1 = min(c0 + per, nchunks);
@@ -159,55 +156,53 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t* __restri
         run += v;
     }
     if (tid == 0) counts[e] = total;
+}
 
-    // The last block to arrive sees every count: offsets and tile list.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = atomicAdd(&sync[1], 1) == E - 1;
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
+// One thread per (token, slot) s: its sorted row is the expert's offset, plus the chunk prefix of earlier
+// chunks, plus the tokens of its own chunk below it in the expert's mask.  Every block first scans the E
+// counts into offsets in LDS (E <= 1024 values: cheaper than a grid-wide hand-off); block 0 also stores
+// the offsets and the tile list.  Threads s < T write the shared expert's row table.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, const uint64_t* __restrict__ chunk_bits,
+                                                      const int32_t* __restrict__ chunk_prefix,
+                                                      const int32_t* __restrict__ counts, int T, int E, int k, int bm,
+                                                      TileRange tr, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted_slots, int32_t* __restrict__ pos,
+                                                      int32_t* __restrict__ row_token, int4* __restrict__ tiles,
+                                                      int32_t* __restrict__ ntiles)
+{
+    __shared__ int cnt[1024], off[1025];
+    __shared__ int scan_lds[5];
+    const int tid = threadIdx.x;
     int carry = 0;
     for (int g0 = 0; g0 < E; g0 += 256) {
         const int g = g0 + tid;
-        const int c = g < E ? __hip_atomic_load(&counts[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        const int c = g < E ? counts[g] : 0;
         int tot;
         const int ex = carry + block_exclusive_scan<256>(c, &tot, scan_lds);
         if (g < E) {
             cnt[g] = c;
             off[g] = ex;
-            offsets[g] = ex;
         }
         carry += tot;
     }
-    if (tid == 0) {
-        off[E] = carry;
-        offsets[E] = carry;
-        sync[1] = 0;
-    }
+    if (tid == 0) off[E] = carry;
     __syncthreads();
-    write_tiles<256>(cnt, off, E, T, k, bm, tr, tiles, sync, scan_lds);
-}
-
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, const uint64_t* __restrict__ chunk_bits,
-                                                     const int32_t* __restrict__ chunk_prefix,
-                                                     const int32_t* __restrict__ offsets, int T, int E, int k,
-                                                     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ pos,
-                                                     int32_t* __restrict__ row_token)
-{
-    const int c = blockIdx.x, lane = threadIdx.x, t = c * 64 + lane;
-    if (t >= T) return;
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-    for (int j = 0; j < k; j++) {
-        const int s = t * k + j;
-        const int e = idx[s];
-        const size_t ce = (size_t)c * E + e;
-        const int p = offsets[e] + chunk_prefix[ce] + __popcll(chunk_bits[ce] & below);
-        pos[s] = p;
-        sorted_slots[p] = s;
-        row_token[p] = t;
+    if (blockIdx.x == 0) {                              // block-uniform
+        for (int g = tid; g <= E; g += 256) offsets[g] = off[g];
+        write_tiles<256>(cnt, off, E, T, k, bm, tr, tiles, ntiles, scan_lds);
     }
-    row_token[T * k + t] = t;
+
+    const int s = blockIdx.x * 256 + tid;
+    if (s < T) row_token[T * k + s] = s;
+    if (s >= T * k) return;
+    const int t = s / k, c = t >> 6, tl = t & 63;
+    const int e = idx[s];
+    const size_t ce = (size_t)c * E + e;
+    const uint64_t below = tl ? (~0ull >> (64 - tl)) : 0ull;
+    const int p = off[e] + chunk_prefix[ce] + __popcll(chunk_bits[ce] & below);
+    pos[s] = p;
+    sorted_slots[p] = s;
+    row_token[p] = t;
 }
 
 bool routing_is_fused(const moe_shape_t& s) { return s.T <= kFusedMaxTokens; }
@@ -230,10 +225,9 @@ hipError_t launch_permute(const moe_shape_t& s, const int32_t* idx, int32_t* cou
                           hipStream_t stream)
 {
     const int T = (int)s.T, E = (int)s.E, k = (int)s.k, nch = (int)ws.nchunks;
-    chunk_scan_kernel<<<E, 256, 0, stream>>>(ws.chunk_counts, nch, E, T, k, bm, tr, ws.chunk_prefix, counts, offsets,
-                                             ws.tiles, ws.sync);
-    scatter_kernel<<<nch, 64, 0, stream>>>(idx, ws.chunk_bits, ws.chunk_prefix, offsets, T, E, k, sorted_slots, pos,
-                                           ws.row_token);
+    chunk_scan_kernel<<<E, 256, 0, stream>>>(ws.chunk_counts, nch, E, ws.chunk_prefix, counts);
+    scatter_kernel<<<(T * k + 255) / 256, 256, 0, stream>>>(idx, ws.chunk_bits, ws.chunk_prefix, counts, T, E, k, bm, tr,
+                                                            offsets, sorted_slots, pos, ws.row_token, ws.tiles, ws.sync);
     return hipGetLastError();
 }
 

@@ -491,32 +491,34 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
 }
 
 // ------------------------------------------------------------------------------------------------
-// Top-k + softmax for many tokens: one wavefront per token, 64 tokens (one chunk) per block of 16
-// wavefronts.  Also records, per chunk, which tokens chose each expert (a 64-bit mask) and how many.
+// Top-k + softmax for many tokens: W lanes per token (16 when E <= 256: four tokens per wavefront at
+// once; a wavefront when E <= 1024), 64 tokens (one chunk) per block of 16 wavefronts.  Also records,
+// per chunk, which tokens chose each expert (a 64-bit mask) and how many.
 // ------------------------------------------------------------------------------------------------
-// NQ: logits per lane (E <= 64 * NQ).
-template <int NQ>
+// NQ: logits per lane (E <= W * NQ).
+template <int W, int NQ>
 __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restrict__ L, const uint8_t* __restrict__ allowed,
                                                             int T, int E, int k,
                                                             int32_t* __restrict__ idx, float* __restrict__ w,
                                                             uint64_t* __restrict__ chunk_bits,
-                                                            int32_t* __restrict__ chunk_counts,
-                                                            int32_t* __restrict__ sync)
+                                                            int32_t* __restrict__ chunk_counts)
 {
+    constexpr int TPW = 64 / W;                        // tokens per wavefront pass
     __shared__ uint32_t bits_lo[1024], bits_hi[1024];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = blockIdx.x;
-    if (c == 0 && threadIdx.x < 4) sync[threadIdx.x] = 0;   // reset the permutation's counters
+    const int sub = lane % W, grp = lane / W;
     for (int e = threadIdx.x; e < E; e += 1024) bits_lo[e] = bits_hi[e] = 0;
     __syncthreads();
-    for (int tl = wave; tl < 64; tl += 16) {
-        const int t = c * 64 + tl;
-        if (t >= T) break;
+    for (int tl0 = wave * TPW; tl0 < 64; tl0 += 16 * TPW) {
+        const int tl = tl0 + grp, t = c * 64 + tl;
+        if (c * 64 + tl0 >= T) break;                  // wavefront-uniform
+        const bool valid = t < T;                      // the W-lane group of a token past T reads token 0
         int my_e;
         float my_w;
-        topk_group<64, NQ>(L + (size_t)t * E, allowed, E, k, lane, my_e, my_w);
-        if (lane < k) {
-            idx[(size_t)t * k + lane] = my_e;
-            w[(size_t)t * k + lane] = my_w;
+        topk_group<W, NQ>(L + (size_t)(valid ? t : 0) * E, allowed, E, k, sub, my_e, my_w);
+        if (valid && sub < k) {
+            idx[(size_t)t * k + sub] = my_e;
+            w[(size_t)t * k + sub] = my_w;
             if (tl < 32) atomicOr(&bits_lo[my_e], 1u << tl);
             else atomicOr(&bits_hi[my_e], 1u << (tl - 32));
         }
@@ -529,15 +531,22 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
     }
 }
 
+#ifndef MOE_TOPK_W16
+#define MOE_TOPK_W16 1
+#endif
+
 hipError_t launch_topk(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
                        const Workspace& ws, hipStream_t stream)
 {
-    if (s.E <= 256)
-        topk_softmax_kernel<4><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, idx,
-                                                                            w, ws.chunk_bits, ws.chunk_counts, ws.sync);
+    if (s.E <= 256 && MOE_TOPK_W16)
+        topk_softmax_kernel<16, 16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
+                                                                                idx, w, ws.chunk_bits, ws.chunk_counts);
+    else if (s.E <= 256)
+        topk_softmax_kernel<64, 4><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
+                                                                               idx, w, ws.chunk_bits, ws.chunk_counts);
     else
-        topk_softmax_kernel<16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k, idx,
-                                                                             w, ws.chunk_bits, ws.chunk_counts, ws.sync);
+        topk_softmax_kernel<64, 16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
+                                                                                idx, w, ws.chunk_bits, ws.chunk_counts);
     return hipGetLastError();
 }
 
