@@ -478,6 +478,21 @@ template <int N> __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 // Barrier without the vmcnt(0) that __syncthreads implies: loads into the other ring buffers stay in flight.
+// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (the count is an immediate: one branch per value).
+template <int LO, int HI> __device__ __forceinline__ void wait_vmcnt_var(int n)
+{
+    if constexpr (LO > HI) {
+        wait_vmcnt<0>();
+    } else if constexpr (LO == HI) {
+        wait_vmcnt<LO>();
+    } else {
+        if (n <= LO) wait_vmcnt<LO>();
+        else wait_vmcnt_var<LO + 1, HI>(n);
+    }
+}
+#ifndef MOE_W_PRO1
+#define MOE_W_PRO1 1
+#endif
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int RB> __device__ __forceinline__ int swzr(int row, int chunk)
@@ -706,8 +721,17 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
         // NSTG - 1 stages are in flight while one is computed and every wait is the same vmcnt.
 #pragma unroll
         for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1));
-        // (a ring of two may skip A loads, so its stages can hold fewer than PERW loads: wait for both)
-        wait_vmcnt<NSTG == 2 ? 0 : (NSTG - 1) * PERW>();
+        // Wait for stage 0 only, its successors staying in flight.  A ring of two may skip A loads: a
+        // wavefront then issues fewer than PERW loads per stage, the same number every stage, so the count
+        // to leave in flight is picked from that (wave-uniform) number.
+        if constexpr (NSTG == 2 && MOE_W_PRO1) {
+            int nld = PERW;
+#pragma unroll
+            for (int p = 0; p < PA; p++) nld -= (NW * p + wave) * RPL >= a_rows;
+            wait_vmcnt_var<PERW - PA, PERW>(nld);
+        } else {
+            wait_vmcnt<NSTG == 2 ? 0 : (NSTG - 1) * PERW>();
+        }
         lds_barrier();
         Frags f0, f1;
         read(0, 0, f0);
