@@ -18,9 +18,10 @@
 // XOR-swizzled by row) and read back as MFMA fragments with 16-byte LDS reads.  Three kernels:
 //   grouped_gemm_kernel    : global loads into registers one stage ahead, then LDS stores (16-row decode
 //                            tiles of every dtype; fp32 128-row tiles);
-//   grouped_gemm_w_kernel  : bf16 128/256-row tiles, one 128 x 128 block of 32x32 MFMAs per wavefront,
+//   grouped_gemm_w_kernel  : bf16 256-row tiles, eight wavefronts of 128 x 64 outputs in 32x32 MFMAs,
 //                            stages copied global -> LDS by direct-to-LDS loads;
-//   grouped_gemm_f8_kernel : fp8 128-row tiles, direct-to-LDS staging of the operands and their scales.
+//   grouped_gemm_f8_kernel : fp8 128- or 256-row tiles, direct-to-LDS staging of the operands and their
+//                            scales.
 // MFMA per element type:
 //   fp32 : v_mfma_f32_16x16x4_f32   (4 per 16-byte fragment; lane group q holds k = 4q + e)
 //   bf16 : v_mfma_f32_16x16x32_bf16 (one per 16-byte fragment), v_mfma_f32_32x32x16_bf16 (wide kernel)
