@@ -56,6 +56,14 @@ def test_workspace_size_rejects_bad_shapes(kw):
     assert B.moe_workspace_size(_shape(**kw)) == 0
 
 
+def test_operands_beyond_32_bit_offsets_are_unsupported():
+    # The GEMMs address x, h and one expert's weights with 32-bit byte offsets: a shape whose x or h
+    # reaches 4 GB is refused (before any launch), one just below is accepted.
+    assert B.moe_workspace_size(_shape(T=299594, d=7168)) == 0          # x: 299594 * 7168 * 2 B >= 4 GB
+    assert B.moe_workspace_size(_shape(T=116509, k=8, inter=2048)) == 0  # h: T * 9 * 2048 * 2 B >= 4 GB
+    assert B.moe_workspace_size(_shape(T=116508, k=8, inter=2048)) > 0   # the largest T below the h limit
+
+
 def _call_forward(shape, ptrs=None, ws_bytes=1 << 30):
     L = B.lib()
     p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(20)] if ptrs is None else ptrs
