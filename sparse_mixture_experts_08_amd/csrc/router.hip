@@ -96,9 +96,9 @@ struct W4 {
 // block still covers their latency.  Both tiles are stored K-major ([i][t], [i][e]) so a thread reads its
 // tokens and four experts of one i with two LDS reads; the x transposing stores put consecutive lanes on
 // consecutive tokens (conflict-free) and the Wg rows are padded so its transposing stores spread over the
-// banks.  Two tokens per thread double the wavefronts of a few-thousand-token call (prefill router
-// 0.42 -> 0.34 ms); four keep more FMAs per LDS read where the wavefronts are plenty.  Per output the K
-// loop runs in order: the chain is exactly the contract's.
+// banks.  Calls above the rotated-operand kernel's range use 64 x 4: with wavefronts plenty, four
+// tokens per thread keep the most FMAs per LDS read.  Per output the K loop runs in order: the chain is
+// exactly the contract's.
 template <typename XT, int BT, int TT>
 __global__ __launch_bounds__(BT / TT * 16) void router_logits_many_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
                                                                           const float* __restrict__ bias, float* __restrict__ L,
@@ -444,11 +444,8 @@ static void launch_few(dim3 grid, const XT* x, const float* Wg, const float* bia
 #ifndef MOE_ROUTER_FEW_MAX_T
 #define MOE_ROUTER_FEW_MAX_T 512
 #endif
-#ifndef MOE_ROUTER_DPP
-#define MOE_ROUTER_DPP 1
-#endif
-#ifndef MOE_ROUTER_BT32_MAX_T
-#define MOE_ROUTER_BT32_MAX_T 8192
+#ifndef MOE_ROUTER_DPP_MAX_T
+#define MOE_ROUTER_DPP_MAX_T 8192
 #endif
 
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
@@ -465,21 +462,12 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
         dim3 grid((E + 15) / 16, (T + 15) / 16);
         if (bf) launch_few<uint16_t, 16>(grid, (const uint16_t*)x, Wg, bias, logits, T, d, E, stream);
         else launch_few<float, 16>(grid, (const float*)x, Wg, bias, logits, T, d, E, stream);
-    } else if (T <= MOE_ROUTER_BT32_MAX_T) {
-#if MOE_ROUTER_DPP
-        dim3 grid_r((E + 31) / 32, (T + 63) / 64);
+    } else if (T <= MOE_ROUTER_DPP_MAX_T) {
+        dim3 grid((E + 31) / 32, (T + 63) / 64);
         if (bf)
-            router_logits_dpp_kernel<uint16_t><<<grid_r, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            router_logits_dpp_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_dpp_kernel<float><<<grid_r, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
-        return hipGetLastError();
-#endif
-        // 32-token tiles: twice the blocks, so a few thousand tokens still put several blocks on a CU
-        dim3 grid((E + 63) / 64, (T + 31) / 32);
-        if (bf)
-            router_logits_many_kernel<uint16_t, 32, 2><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
-        else
-            router_logits_many_kernel<float, 32, 2><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            router_logits_dpp_kernel<float><<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     } else {
         dim3 grid((E + 63) / 64, (T + 63) / 64);
         if (bf)
