@@ -1,6 +1,6 @@
 """Summarise the rocprofv3 runs of one bench.py workload into profiles/.
 
-python rocprof_summary.py WORKLOAD VARIANT TRACE_DIR FETCH_DIR WRITE_DIR
+python rocprof_summary.py WORKLOAD VARIANT TRACE_DIR FETCH_DIR WRITE_DIR [CLOCK_DIR]
 
 TRACE_DIR holds the CSV output of `rocprofv3 --kernel-trace --stats -f csv -o run`, FETCH_DIR and WRITE_DIR
 that of `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` over a bench.py run that ends with one plain
@@ -8,7 +8,9 @@ that of `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` over a bench.py run th
 (kernel durations and HBM bytes per dispatch) and records the grouped GEMMs' bytes per launch, scaled by
 what the counters read for the known-size copy, in profiles/traffic.json under the fingerprint of the GEMM
 code they were taken on (sha256[:16] of csrc/gemm.hip without comments or whitespace; bench.py reports
-them only while it matches).
+them only while it matches).  CLOCK_DIR, if given, holds a `--pmc GRBM_COUNT` run: GRBM_COUNT ticks once per
+shader clock in each XCD, so per dispatch GRBM_COUNT / duration / XCD count is the average shader clock the
+kernel ran at (the chip lowers it below its 2.4 GHz peak under load).
 """
 import csv
 import glob
@@ -42,6 +44,17 @@ def _counter(d, name):
     return {k: ((max(v), 1) if "copyBuffer" in k else (sum(v) / len(v), len(v))) for k, v in vals.items()}
 
 
+def _clocks(d):
+    """Average shader clock (GHz) per dispatch, by kernel name, from a --pmc GRBM_COUNT run."""
+    nx = max(int(r.get("Num_Xcc") or 0) for r in _csv(d, "agent_info.csv"))
+    vals = defaultdict(list)
+    for r in _csv(d, "counter_collection.csv"):
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if r["Counter_Name"] == "GRBM_COUNT" and dur > 0:
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]) / dur / nx)
+    return nx, {k: (sum(v) / len(v), min(v), max(v), len(v)) for k, v in vals.items()}
+
+
 def gemm_role(kernel):
     """'up_gemm' / 'down_gemm' for the grouped GEMM kernels, else None."""
     m = re.search(r"grouped_gemm_(w_|f8_)?kernel<([^>]*)>", kernel)
@@ -54,6 +67,7 @@ def gemm_role(kernel):
 
 def main():
     workload, variant, trace_dir, fetch_dir, write_dir = sys.argv[1:6]
+    clock_dir = sys.argv[6] if len(sys.argv) > 6 else None
     key = workload if variant == "layer" else f"{workload}/{variant}"
     stats = _csv(trace_dir, "kernel_stats.csv")
     fetch, write = _counter(fetch_dir, "FETCH_SIZE"), _counter(write_dir, "WRITE_SIZE")
@@ -76,7 +90,11 @@ def main():
         lines.append(f'rocprofv3 --pmc {c} --kernel-include-regex "moe::|copyBuffer" -f csv -d '
                      f"$OUT/{c} -o run -- {bench} --steps 1 --warmup 1 --no-cpu-baseline "
                      "--copy-calibration-mib 1024")
-    lines.append(f"python3 $R/rocprof_summary.py {workload} {variant} $OUT/trace $OUT/FETCH_SIZE $OUT/WRITE_SIZE")
+    if clock_dir:
+        lines.append(f'rocprofv3 --pmc GRBM_COUNT --kernel-include-regex "moe::" -f csv -d $OUT/GRBM_COUNT -o run '
+                     f"-- {bench} --steps 2 --warmup 1 --no-cpu-baseline")
+    lines.append(f"python3 $R/rocprof_summary.py {workload} {variant} $OUT/trace $OUT/FETCH_SIZE $OUT/WRITE_SIZE"
+                 + (" $OUT/GRBM_COUNT" if clock_dir else ""))
     lines += ["```", "", "## Kernel durations (--kernel-trace --stats; every dispatch in the run, including the "
               "staged pass)", "", "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in moe:
@@ -101,6 +119,17 @@ def main():
         role = gemm_role(k)
         if role:
             rec[role] = {"kernel": k, "bytes": (rb + wb) * 1e9}
+    if clock_dir:
+        nx, clk = _clocks(clock_dir)
+        lines += ["", "## Average shader clock per dispatch (--pmc GRBM_COUNT / duration / "
+                  f"{nx} XCDs; peak 2.4 GHz)", "",
+                  "Kernels of a few microseconds read high: the counter window is wider than the kernel.", "",
+                  "| kernel | dispatches | average GHz | min GHz | max GHz |", "|---|---|---|---|---|"]
+        traced = [r["Name"] for r in moe if r["Name"] in clk]
+        order = traced + sorted(k for k in clk if k not in traced)
+        for k in order:
+            a, lo, hi, n = clk[k]
+            lines.append(f"| `{k}` | {n} | {a:.2f} | {lo:.2f} | {hi:.2f} |")
     lines += ["", "GEMM code fingerprint when measured (sha256[:16] of csrc/gemm.hip without comments or whitespace): "
               f"`{rec['gemm_code_sha256_16']}`",
               ""]
