@@ -479,21 +479,6 @@ template <int N> __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 // Barrier without the vmcnt(0) that __syncthreads implies: loads into the other ring buffers stay in flight.
-// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (the count is an immediate: one branch per value).
-template <int LO, int HI> __device__ __forceinline__ void wait_vmcnt_var(int n)
-{
-    if constexpr (LO > HI) {
-        wait_vmcnt<0>();
-    } else if constexpr (LO == HI) {
-        wait_vmcnt<LO>();
-    } else {
-        if (n <= LO) wait_vmcnt<LO>();
-        else wait_vmcnt_var<LO + 1, HI>(n);
-    }
-}
-#ifndef MOE_W_PRO1
-#define MOE_W_PRO1 1
-#endif
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int RB> __device__ __forceinline__ int swzr(int row, int chunk)
@@ -637,18 +622,18 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
     }
     __syncthreads();                                   // the row table is dead from here
 
-    // 32-row MFMA blocks holding tile rows: per wavefront (wave-uniform) and for the whole tile.  Blocks
-    // past the tile's end get no MFMAs and no fragment reads, and with a ring of two the A rows past the
-    // last computed block are not loaded either (with deeper rings every stage keeps the same number of
-    // loads per wavefront, which the vmcnt accounting below relies on).
+    // 32-row MFMA blocks holding tile rows (per wavefront, wave-uniform).  Blocks past the tile's end get
+    // no MFMAs and no fragment reads; their A rows are still copied (the row table repeats the tile's first
+    // row there, so the copies hit in cache): every wavefront issues the same loads each stage with no
+    // branch between them, which costs less than the copies it would save (prefill up GEMM 3.47 -> 3.44 ms).
     const int nrb = max(0, min(4, (rows - wm0 + 31) / 32));
-    const int a_rows = NSTG == 2 ? min(BM, (rows + 31) / 32 * 32) : BM;
 
     // K stages walked from a start rotated by the n-block (as in grouped_gemm_kernel), in a fixed order.
     const int nstages = K / (RB / 2);
     const int kshift = (nb * g.krot) % nstages;
     const uint32_t ring0 = lds_addr(ring);
-    auto issue = [&](int buf, int s) {
+    // Stage s into ring buffer buf: this wavefront's loads p0 .. p1 - 1.
+    auto issue = [&](int buf, int s, int p0, int p1) {
         const int ks = s + kshift >= nstages ? s + kshift - nstages : s + kshift;
         const int64_t koff = (int64_t)ks * RB;
         const uint8_t* a = g.A + koff;
@@ -656,8 +641,7 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
         const uint8_t* b3 = W3 + koff;
         const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
 #pragma unroll
-        for (int p = 0; p < PERW; p++) {
-            if (p < PA && (NW * p + wave) * RPL >= a_rows) continue;
+        for (int p = p0; p < p1; p++) {
             dma16(p < PA ? a : p < PA + PB1 ? b1 : b3, off[p], dst + p * NW * 1024);
         }
     };
@@ -720,19 +704,17 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
         // stage s (all its fragments read) stage s + 1 is awaited and published, and stage s's buffer is
         // refilled with stage s + NSTG (past the end: the last stage again, into a buffer nobody reads), so
         // NSTG - 1 stages are in flight while one is computed and every wait is the same vmcnt.
+        // A freed buffer is refilled around the K step that follows the barrier: the up GEMM issues half of
+        // the stage's loads before that step and half after it (prefill up GEMM 3.44 -> 3.415 ms), the down
+        // GEMM all of them before it (split, its skewed-workload time grows by 1 %).
+        auto refill = [&](int b, int st, auto&& step) {
+            issue(b, st, 0, UP ? PERW / 2 : PERW);
+            step();
+            if constexpr (UP) issue(b, st, PERW / 2, PERW);
+        };
 #pragma unroll
-        for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1));
-        // Wait for stage 0 only, its successors staying in flight.  A ring of two may skip A loads: a
-        // wavefront then issues fewer than PERW loads per stage, the same number every stage, so the count
-        // to leave in flight is picked from that (wave-uniform) number.
-        if constexpr (NSTG == 2 && MOE_W_PRO1) {
-            int nld = PERW;
-#pragma unroll
-            for (int p = 0; p < PA; p++) nld -= (NW * p + wave) * RPL >= a_rows;
-            wait_vmcnt_var<PERW - PA, PERW>(nld);
-        } else {
-            wait_vmcnt<NSTG == 2 ? 0 : (NSTG - 1) * PERW>();
-        }
+        for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1), 0, PERW);
+        wait_vmcnt<(NSTG - 1) * PERW>();               // stage 0 only, its successors stay in flight
         lds_barrier();
         Frags f0, f1;
         read(0, 0, f0);
@@ -745,14 +727,12 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
                 kstep(f0, buf, 3, f1);
                 wait_vmcnt<(NSTG - 2) * PERW>();
                 lds_barrier();
-                issue(buf, min(s + NSTG, nstages - 1));
-                kstep(f1, nbuf, 0, f0);
+                refill(buf, min(s + NSTG, nstages - 1), [&] { kstep(f1, nbuf, 0, f0); });
             } else {
                 kstep(f0, buf, 1, f1);
                 wait_vmcnt<(NSTG - 2) * PERW>();
                 lds_barrier();
-                issue(buf, min(s + NSTG, nstages - 1));
-                kstep(f1, nbuf, 0, f0);
+                refill(buf, min(s + NSTG, nstages - 1), [&] { kstep(f1, nbuf, 0, f0); });
             }
             buf = nbuf;
         }
