@@ -780,12 +780,14 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 // keeps the register footprint fixed: B fragments of the stage stay in registers, A fragments and the
 // row scales are read one row block ahead; with more than 64 accumulator VGPRs a row block's MFMAs also
 // wait for the rescaling of the previous block's results, so only one block's MFMA results are live and
-// a 128 x 64 wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.
-template <bool UP, int WM, int WN, int BN>
+// a 128 x 64 wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.  mid() runs once the
+// second row block's MFMAs are issued: the kernel issues the second half of a ring refill there.
+template <bool UP, int WM, int WN, int BN, typename MID>
 __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_lds, const float* sA_lds, float sb1,
                                        float sb3, int wm0, int wn0, int lane, f32x4 (&acc1)[WM][WN],
-                                       f32x4 (&acc3)[WM][WN])
+                                       f32x4 (&acc3)[WM][WN], MID&& mid)
 {
+    static_assert(WM >= 2, "mid() runs after the second row block");
     const int r16 = lane & 15, q = lane >> 4;
     constexpr bool TIGHT = WM * WN * (UP ? 2 : 1) > 16;  // more than 64 accumulator VGPRs
     auto frag = [&](const uint8_t* base, int row) {
@@ -823,6 +825,7 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                     if constexpr (UP)
                         pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
                 }
+                if (i == 1) mid();
                 if (i + 1 < WM) {
                     a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
                     sa_next = scales(i + 1);
@@ -883,6 +886,7 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                 for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * s3[r];
             }
         }
+        if (i == 1) mid();
         a = a_next;
         sa = sa_next;
     }
@@ -968,16 +972,17 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     const int nstages = K / 128;
     const int kshift = (nb * g.krot) % nstages;
     const uint32_t ring0 = lds_addr(ring), scl0 = lds_addr(&scl[0][0]);
-    auto issue = [&](int buf, int s) {
+    // Stage s into ring buffer buf: this wavefront's operand loads p0 .. p1 - 1, and its scale load if asked.
+    auto issue = [&](int buf, int s, int p0, int p1, bool with_scales) {
         const int ks = s + kshift >= nstages ? s + kshift - nstages : s + kshift;
         const int64_t koff = (int64_t)ks * 128;
         const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
 #pragma unroll
-        for (int p = 0; p < PERW; p++) dma16((p < PA ? g.A : p < PA + PB1 ? W1 : W3) + koff, off[p], dst + p * NW * 1024);
+        for (int p = p0; p < p1; p++) dma16((p < PA ? g.A : p < PA + PB1 ? W1 : W3) + koff, off[p], dst + p * NW * 1024);
         const uint8_t* sb = wave < SW ? (const uint8_t*)(g.As + ks)
                           : wave == SW ? (const uint8_t*)(W1s + ks)
                           : (UP && wave == SW + 1) ? (const uint8_t*)(W3s + ks) : (const uint8_t*)W1s;
-        dma4(sb, soff, scl0 + (buf * NW * 64 + wave * 64) * 4);
+        if (with_scales) dma4(sb, soff, scl0 + (buf * NW * 64 + wave * 64) * 4);
     };
 
     f32x4 acc1[WM][WN], acc3[WM][WN];
@@ -988,19 +993,25 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
 
     const int cb = wn0 / 128;                          // the wavefront's weight block within the n-block
 #pragma unroll
-    for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1));
+    for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1), 0, PERW, true);
     wait_vmcnt<(NSTG - 1) * NL>();
     lds_barrier();
-    int buf = 0;
+    // A freed buffer is refilled in two halves: the first right after the barrier, the rest (with the
+    // scales) from inside the next stage's MFMAs, so no wavefront stalls on a burst of loads before its
+    // MFMAs (fp8 up GEMM 11.48 -> 11.19 ms).  Every load of the refill still precedes the next wait.
+    int buf = 0, pbuf = -1, pst = 0;
     for (int s = 0; s < nstages; s++) {
         const float* sc = scl[buf];
         const uint8_t* st = ring + buf * STAGE;
         mma_f8<UP, WM, WN, BN>(st, st + BM * 128, sc, sc[BM + cb], UP ? sc[BM + 64 + cb] : 0.f, wm0, wn0, lane, acc1,
-                               acc3);
+                               acc3, [&] { if (pbuf >= 0) issue(pbuf, pst, PERW / 2, PERW, true); });
+        pbuf = -1;
         if (s + 1 < nstages) {
             wait_vmcnt<(NSTG - 2) * NL>();             // stage s + 1 has landed
             lds_barrier();                             // ... for every wavefront; stage s is read
-            issue(buf, min(s + NSTG, nstages - 1));    // past the end: the last stage again (never read)
+            pst = min(s + NSTG, nstages - 1);          // past the end: the last stage again (never read)
+            issue(buf, pst, 0, PERW / 2, false);
+            pbuf = buf;
             buf = buf + 1 == NSTG ? 0 : buf + 1;
         }
     }
