@@ -780,14 +780,17 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 // keeps the register footprint fixed: B fragments of the stage stay in registers, A fragments and the
 // row scales are read one row block ahead; with more than 64 accumulator VGPRs a row block's MFMAs also
 // wait for the rescaling of the previous block's results, so only one block's MFMA results are live and
-// a 128 x 64 wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.  mid() runs once the
-// second row block's MFMAs are issued: the kernel issues the second half of a ring refill there.
+// a 128 x 64 wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.  mid() runs once row
+// block MID_AT's MFMAs are issued: the kernel issues the second half of a ring refill there (the up GEMM
+// after its fourth row block, the down GEMM after its first; against the second for both: up 11.40 ->
+// 11.24 ms, down 5.88 -> 5.72 ms).
 template <bool UP, int WM, int WN, int BN, typename MID>
 __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_lds, const float* sA_lds, float sb1,
                                        float sb3, int wm0, int wn0, int lane, f32x4 (&acc1)[WM][WN],
                                        f32x4 (&acc3)[WM][WN], MID&& mid)
 {
-    static_assert(WM >= 2, "mid() runs after the second row block");
+    constexpr int MID_AT = UP ? 3 : 0;
+    static_assert(WM > MID_AT, "mid() runs inside the row-block loop");
     const int r16 = lane & 15, q = lane >> 4;
     constexpr bool TIGHT = WM * WN * (UP ? 2 : 1) > 16;  // more than 64 accumulator VGPRs
     auto frag = [&](const uint8_t* base, int row) {
@@ -825,7 +828,7 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                     if constexpr (UP)
                         pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
                 }
-                if (i == 1) mid();
+                if (i == MID_AT) mid();
                 if (i + 1 < WM) {
                     a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
                     sa_next = scales(i + 1);
@@ -886,7 +889,7 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                 for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * s3[r];
             }
         }
-        if (i == 1) mid();
+        if (i == MID_AT) mid();
         a = a_next;
         sa = sa_next;
     }
@@ -998,7 +1001,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     lds_barrier();
     // A freed buffer is refilled in two halves: the first right after the barrier, the rest (with the
     // scales) from inside the next stage's MFMAs, so no wavefront stalls on a burst of loads before its
-    // MFMAs (fp8 up GEMM 11.48 -> 11.19 ms).  Every load of the refill still precedes the next wait.
+    // MFMAs (fp8 up GEMM 11.48 -> 11.19 ms with the second half after the second row block).  Every load
+    // of the refill still precedes the next wait.
     int buf = 0, pbuf = -1, pst = 0;
     for (int s = 0; s < nstages; s++) {
         const float* sc = scl[buf];
