@@ -625,7 +625,8 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
     // 32-row MFMA blocks holding tile rows (per wavefront, wave-uniform).  Blocks past the tile's end get
     // no MFMAs and no fragment reads; their A rows are still copied (the row table repeats the tile's first
     // row there, so the copies hit in cache): every wavefront issues the same loads each stage with no
-    // branch between them, which costs less than the copies it would save (prefill up GEMM 3.47 -> 3.44 ms).
+    // branch between them, which was no slower than the copies it saved (prefill up GEMM 3.47 -> 3.44 ms,
+    // within the kernel's run-to-run spread) and keeps one vmcnt value for every wavefront.
     const int nrb = max(0, min(4, (rows - wm0 + 31) / 32));
 
     // K stages walked from a start rotated by the n-block (as in grouped_gemm_kernel), in a fixed order.
@@ -705,8 +706,8 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
         // refilled with stage s + NSTG (past the end: the last stage again, into a buffer nobody reads), so
         // NSTG - 1 stages are in flight while one is computed and every wait is the same vmcnt.
         // A freed buffer is refilled around the K step that follows the barrier: the up GEMM issues half of
-        // the stage's loads before that step and half after it (prefill up GEMM 3.44 -> 3.415 ms), the down
-        // GEMM all of them before it (split, its skewed-workload time grows by 1 %).
+        // the stage's loads before that step and half after it (prefill up GEMM 3.44 -> 3.415 ms, within
+        // run-to-run spread), the down GEMM all of them before it (split, its skewed time grows by 1 %).
         auto refill = [&](int b, int st, auto&& step) {
             issue(b, st, 0, UP ? PERW / 2 : PERW);
             step();
