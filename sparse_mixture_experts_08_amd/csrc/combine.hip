@@ -120,9 +120,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
 }
 
-#ifndef MOE_COMBINE_THREADS
-#define MOE_COMBINE_THREADS 128
-#endif
+static constexpr int COMBINE_THREADS = 128;
 
 // Grid: with few tokens one block per (token, column chunk), so decode-sized T still spreads over the
 // CUs; with many tokens one block per token, which amortises the slot sort over the row.  128-thread
@@ -138,15 +136,15 @@ template <bool ACT_BF16>
 static void launch_combine_t(const moe_shape_t& s, const int32_t* pos, const float* w, const Workspace& ws, void* y,
                              hipStream_t stream)
 {
-    const dim3 grid = combine_grid(s, MOE_COMBINE_THREADS);
+    const dim3 grid = combine_grid(s, COMBINE_THREADS);
     const int T = (int)s.T, d = (int)s.d, k = (int)s.k;
     const uint8_t* rows = (const uint8_t*)ws.y_rows;
     uint8_t* out = (uint8_t*)y;
     switch (k) {
-    case 4: combine_kernel<ACT_BF16, 4><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
-    case 6: combine_kernel<ACT_BF16, 6><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
-    case 8: combine_kernel<ACT_BF16, 8><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
-    default: combine_kernel<ACT_BF16, 0><<<grid, MOE_COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 4: combine_kernel<ACT_BF16, 4><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 6: combine_kernel<ACT_BF16, 6><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 8: combine_kernel<ACT_BF16, 8><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    default: combine_kernel<ACT_BF16, 0><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
     }
 }
 

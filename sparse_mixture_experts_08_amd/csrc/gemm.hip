@@ -1086,22 +1086,12 @@ static void launch_one(GemmArgs a, hipStream_t stream)
 
 // K-stage rotation per n-block: the down GEMM (rows of inter elements) and the large-tile up GEMMs gain
 // from it; the up GEMM with 16-row tiles already streams at the HBM ceiling without it.
-#ifndef MOE_KROT_UP16
-#define MOE_KROT_UP16 0
-#endif
-#ifndef MOE_KROT_UP
-#define MOE_KROT_UP 3
-#endif
-#ifndef MOE_KROT_WDN
-#define MOE_KROT_WDN 3      // wide-kernel down GEMM (rotations 0 / 1 / 5 / 7 / 13 measured slower)
-#endif
-#ifndef MOE_KROT_DN
-#define MOE_KROT_DN 1
-#endif
+static constexpr int KROT_UP16 = 0;
+static constexpr int KROT_UP = 3;
+static constexpr int KROT_WDN = 3;   // wide-kernel down GEMM (rotations 0 / 1 / 5 / 7 / 13 measured slower)
+static constexpr int KROT_DN = 1;
 // Tiles per XCD group of the large-tile block order (see grouped_gemm_kernel).
-#ifndef MOE_GROUP_M
-#define MOE_GROUP_M 8
-#endif
+static constexpr int GROUP_M = 8;
 
 // bf16 256-row tiles: 128-byte K stages in a ring of two (64-byte stages in deeper rings request twice
 // the lines and measured slower), eight wavefronts (four, one per SIMD with 128 x 128 each, measured
@@ -1123,25 +1113,9 @@ static void launch_f8(GemmArgs a, hipStream_t stream)
 }
 
 // 16-row tiles (bf16): output features per block, wavefronts, minimum wavefronts per SIMD.  inter and
-// inter_shared must be multiples of MOE_SMALL_UP_BN.
-#ifndef MOE_SMALL_UP_BN
-#define MOE_SMALL_UP_BN 64
-#endif
-#ifndef MOE_SMALL_UP_WAVES
-#define MOE_SMALL_UP_WAVES 4
-#endif
-#ifndef MOE_SMALL_UP_MINW
-#define MOE_SMALL_UP_MINW 1
-#endif
-#ifndef MOE_SMALL_DN_BN
-#define MOE_SMALL_DN_BN 64
-#endif
-#ifndef MOE_SMALL_DN_WAVES
-#define MOE_SMALL_DN_WAVES 4
-#endif
-#ifndef MOE_SMALL_DN_MINW
-#define MOE_SMALL_DN_MINW 1
-#endif
+// inter_shared must be multiples of SMALL_UP_BN.
+static constexpr int SMALL_UP_BN = 64, SMALL_UP_WAVES = 4, SMALL_UP_MINW = 1;
+static constexpr int SMALL_DN_BN = 64, SMALL_DN_WAVES = 4, SMALL_DN_MINW = 1;
 
 // Common fields of both GEMMs' arguments.
 static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws, int e_base)
@@ -1152,7 +1126,7 @@ static GemmArgs base_args(const moe_shape_t& s, const Workspace& ws, int e_base)
     a.ntiles = ws.sync;
     a.max_tiles = (int)ws.max_tiles;
     a.E = (int)s.E;
-    a.group_m = tile_rows(s) == 16 ? 0 : MOE_GROUP_M;
+    a.group_m = tile_rows(s) == 16 ? 0 : GROUP_M;
     return a;
 }
 
@@ -1193,7 +1167,7 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
     up.N_s = n_shared;
     up.K_r = up.K_s = (int)s.d;
     const int bm = tile_rows(s);
-    up.krot = bm == 16 ? MOE_KROT_UP16 : MOE_KROT_UP;
+    up.krot = bm == 16 ? KROT_UP16 : KROT_UP;
     if (fp8) {
         up.n_blocks = (int)(ws.inter_max / 128);
         if (bm == 16) launch_one<ET_FP8, true, true, 16, 128, 1, 4>(up, stream);
@@ -1204,8 +1178,8 @@ hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, c
         if (bm == 16) launch_one<ET_F32, true, false, 16, 64, 1, 4>(up, stream);
         else launch_one<ET_F32, true, false, 128, 64, 2, 2>(up, stream);
     } else if (bm == 16) {
-        up.n_blocks = (int)(ws.inter_max / MOE_SMALL_UP_BN);
-        launch_one<ET_BF16, true, true, 16, MOE_SMALL_UP_BN, 1, MOE_SMALL_UP_WAVES, 2, MOE_SMALL_UP_MINW>(up, stream);
+        up.n_blocks = (int)(ws.inter_max / SMALL_UP_BN);
+        launch_one<ET_BF16, true, true, 16, SMALL_UP_BN, 1, SMALL_UP_WAVES, 2, SMALL_UP_MINW>(up, stream);
     } else {
         up.n_blocks = (int)(ws.inter_max / 128);
         launch_w<true>(up, stream);
@@ -1235,7 +1209,7 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     dn.N_r = dn.N_s = (int)s.d;
     dn.K_r = (int)s.inter;
     dn.K_s = n_shared;
-    dn.krot = MOE_KROT_DN;
+    dn.krot = KROT_DN;
     const int bm = tile_rows(s);
     // With at most one tile per expert on average no weight panel is shared between tiles: walk each
     // tile's n-blocks together instead, so its h rows are fetched once into L2.
@@ -1246,9 +1220,9 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
         dn.n_blocks = (int)(s.d / 64);
         if (fp8) launch_one<ET_FP8, false, true, 16, 64, 1, 4>(dn, stream);
         else if (f32) launch_one<ET_F32, false, false, 16, 64, 1, 4>(dn, stream);
-        else if (s.d % MOE_SMALL_DN_BN == 0) {
-            dn.n_blocks = (int)(s.d / MOE_SMALL_DN_BN);
-            launch_one<ET_BF16, false, true, 16, MOE_SMALL_DN_BN, 1, MOE_SMALL_DN_WAVES, 2, MOE_SMALL_DN_MINW>(dn, stream);
+        else if (s.d % SMALL_DN_BN == 0) {
+            dn.n_blocks = (int)(s.d / SMALL_DN_BN);
+            launch_one<ET_BF16, false, true, 16, SMALL_DN_BN, 1, SMALL_DN_WAVES, 2, SMALL_DN_MINW>(dn, stream);
         } else launch_one<ET_BF16, false, true, 16, 64, 1, 4>(dn, stream);
     } else if (fp8) {
         dn.n_blocks = (int)(s.d / (wide ? 256 : 128));
@@ -1259,7 +1233,7 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
         launch_one<ET_F32, false, false, 128, 128, 2, 2>(dn, stream);
     } else if (wide) {
         dn.n_blocks = (int)(s.d / 256);
-        dn.krot = MOE_KROT_WDN;
+        dn.krot = KROT_WDN;
         launch_w<false>(dn, stream);
     } else {
         dn.n_blocks = (int)(s.d / 128);

@@ -10,8 +10,9 @@
 // (token, expert) output keeps exactly that chain and the routing decision is a deterministic function
 // of x, Wg and bias.
 //
-// Top-k.  One wavefront per token; each lane holds E/64 logits as 64-bit keys (order-preserving bits of
-// the logit, then the complemented expert index), so a wave-wide max picks the largest logit and, among
+// Top-k.  A group of lanes per token (16 lanes when E <= 256, four tokens per wavefront; a whole wavefront
+// when E <= 1024); each lane holds its share of the logits as 64-bit keys (order-preserving bits of the
+// logit, then the complemented expert index), so a group-wide max picks the largest logit and, among
 // equal logits, the lower expert index.  k rounds give the experts in descending-logit order.
 #include <type_traits>
 
@@ -225,9 +226,6 @@ __device__ __forceinline__ void fma_rotated8(float (&a)[8], float4 w, float4 x)
 #undef MOE_DPP_FMA7
 #undef MOE_DPP_FMA
 
-#ifndef MOE_DPP_BK
-#define MOE_DPP_BK 64
-#endif
 
 // Mid-sized T: per 16-lane row an outer product of 16 tokens x 8 experts with one LDS read per operand
 // per lane and K step.  Lane l reads x of token l and the gate row of expert l % 8 and, through
@@ -245,7 +243,7 @@ __global__ __launch_bounds__(256) void router_logits_dpp_kernel(const XT* __rest
                                                                const float* __restrict__ bias, float* __restrict__ L,
                                                                int T, int d, int E)
 {
-    constexpr int BT = 64, BE = 32, BK = MOE_DPP_BK, PAD = 4, NQ = BK / 32;
+    constexpr int BT = 64, BE = 32, BK = 64, PAD = 4, NQ = BK / 32;
     static_assert(BK % 32 == 0, "whole 32-wide loader steps");
     __shared__ __attribute__((aligned(16))) float xs[2][BT][BK + PAD];
     __shared__ __attribute__((aligned(16))) float ws[2][BE][BK + PAD];
@@ -441,12 +439,10 @@ static void launch_few(dim3 grid, const XT* x, const float* Wg, const float* bia
         router_logits_few_kernel<XT, TPB, 128><<<grid, TPB * 16, 0, stream>>>(x, Wg, bias, logits, T, d, E);
 }
 
-#ifndef MOE_ROUTER_FEW_MAX_T
-#define MOE_ROUTER_FEW_MAX_T 512
-#endif
-#ifndef MOE_ROUTER_DPP_MAX_T
-#define MOE_ROUTER_DPP_MAX_T 8192
-#endif
+// Router kernel by token count: the few-token kernel up to 512 tokens, the DPP row-rotation kernel up to
+// 8192, the 64 x 64 register tiles above.
+static constexpr int ROUTER_FEW_MAX_T = 512;
+static constexpr int ROUTER_DPP_MAX_T = 8192;
 
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
                                 float* logits, hipStream_t stream)
@@ -458,11 +454,11 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
         dim3 grid((E + 15) / 16, (T + 7) / 8);
         if (bf) launch_few<uint16_t, 8>(grid, (const uint16_t*)x, Wg, bias, logits, T, d, E, stream);
         else launch_few<float, 8>(grid, (const float*)x, Wg, bias, logits, T, d, E, stream);
-    } else if (T <= MOE_ROUTER_FEW_MAX_T) {
+    } else if (T <= ROUTER_FEW_MAX_T) {
         dim3 grid((E + 15) / 16, (T + 15) / 16);
         if (bf) launch_few<uint16_t, 16>(grid, (const uint16_t*)x, Wg, bias, logits, T, d, E, stream);
         else launch_few<float, 16>(grid, (const float*)x, Wg, bias, logits, T, d, E, stream);
-    } else if (T <= MOE_ROUTER_DPP_MAX_T) {
+    } else if (T <= ROUTER_DPP_MAX_T) {
         dim3 grid((E + 31) / 32, (T + 63) / 64);
         if (bf)
             router_logits_dpp_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
@@ -519,19 +515,12 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
     }
 }
 
-#ifndef MOE_TOPK_W16
-#define MOE_TOPK_W16 1
-#endif
-
 hipError_t launch_topk(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
                        const Workspace& ws, hipStream_t stream)
 {
-    if (s.E <= 256 && MOE_TOPK_W16)
+    if (s.E <= 256)
         topk_softmax_kernel<16, 16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
                                                                                 idx, w, ws.chunk_bits, ws.chunk_counts);
-    else if (s.E <= 256)
-        topk_softmax_kernel<64, 4><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
-                                                                               idx, w, ws.chunk_bits, ws.chunk_counts);
     else
         topk_softmax_kernel<64, 16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
                                                                                 idx, w, ws.chunk_bits, ws.chunk_counts);

@@ -207,3 +207,54 @@ def test_combine_is_weighted_sum_of_experts_plus_shared(oracle):
             ref[t] += float(r["w"][t, j]) * ye[0]
     rel = float((torch.from_numpy(out).double() - ref).norm() / ref.norm())
     assert rel <= 1e-5, rel
+
+
+@pytest.mark.parametrize("wl", [
+    W.Workload("combine-bf16-k3", 40, 256, 8, 3, 128, 128, BF16, BF16),
+    W.Workload("combine-bf16-k5", 33, 256, 12, 5, 256, 128, BF16, BF16),
+    W.Workload("combine-fp8-k4", 27, 256, 8, 4, 128, 128, BF16, FP8),
+], ids=lambda w: w.name)
+def test_combine_bf16_follows_the_page_loop_bitwise(oracle, wl):
+    # The MoE forward excerpt of "DeepSeek-V3.2-Exp / Mixture of experts": y = zeros(fp32); for each
+    # expert i ascending with tokens, idx, top = where(indices == i); y[idx] += expert(x[idx]) *
+    # weights[idx, top, None]; then y += shared_experts(x).  Written here in torch with the expert outputs
+    # in the activation dtype (bf16 tensors; bf16 * fp32 promotes to an fp32 product), the weights from
+    # the oracle's routing (k >= 3, all different from 0 and 1), and the per-expert outputs from one
+    # single-expert oracle call each (pinned by the dense reduction above).  The oracle's fp32 output must
+    # equal the loop bitwise, and its bf16 y the loop's y rounded once.
+    inp = W.generate(wl, seed=21, device="cpu")
+    r, out, y = _run_oracle(oracle, wl, inp)
+    w = torch.from_numpy(r["w"])
+    assert wl.k >= 3 and bool(((w > 0) & (w < 1)).all())
+    indices = torch.from_numpy(r["idx"]).long()
+    xv = inp["x"].float().numpy()
+    shp = wl.shape()
+
+    def expert_out(w1, w3, w2, s1, s3, s2, n_inter):
+        sc = [None if s is None else W.to_numpy(s) for s in (s1, s3, s2)]
+        ye = oracle.swiglu_rows(shp, xv, W.to_numpy(w1), W.to_numpy(w3), W.to_numpy(w2), n_inter, *sc)
+        return torch.from_numpy(ye).to(torch.bfloat16)          # exact: the values are bf16 already
+
+    fp8 = wl.w_dtype == FP8
+    ys = torch.zeros((wl.T, wl.d), dtype=torch.float32)
+    for i in range(wl.E):
+        idx, top = torch.where(indices == i)
+        if idx.numel() == 0:
+            continue
+        s = [inp[n][i] if fp8 else None for n in ("W1s", "W3s", "W2s")]
+        ye = expert_out(inp["W1"][i], inp["W3"][i], inp["W2"][i], *s, wl.inter)
+        assert ye.dtype == torch.bfloat16
+        ys[idx] += ye[idx] * w[idx, top, None]
+    s = [inp[n] if fp8 else None for n in ("S1s", "S3s", "S2s")]
+    ys += expert_out(inp["S1"], inp["S3"], inp["S2"], *s, wl.inter_shared)
+    assert np.array_equal(out.view(np.uint32), ys.numpy().view(np.uint32))
+    assert np.array_equal(y, W.to_numpy(ys.to(torch.bfloat16)))
+    # the pin is sharp: rounding each product, or the running sum, to bf16 changes the result
+    alt = torch.zeros_like(ys)
+    for i in range(wl.E):
+        idx, top = torch.where(indices == i)
+        if idx.numel():
+            s = [inp[n][i] if fp8 else None for n in ("W1s", "W3s", "W2s")]
+            ye = expert_out(inp["W1"][i], inp["W3"][i], inp["W2"][i], *s, wl.inter)
+            alt[idx] += (ye[idx] * w[idx, top, None]).to(torch.bfloat16).float()
+    assert not np.array_equal(out.view(np.uint32), alt.numpy().view(np.uint32))
