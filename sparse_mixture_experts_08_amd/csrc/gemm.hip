@@ -473,6 +473,17 @@ template <int N> struct IntC {
     static constexpr int value = N;
 };
 
+// f(IntC<n>{}) for a runtime n in [0, N] (n outside: f(IntC<0>{})).
+template <int N, typename F> __device__ __forceinline__ void with_count(int n, F&& f)
+{
+    if constexpr (N == 0) {
+        f(IntC<0>{});
+    } else {
+        if (n == N) f(IntC<N>{});
+        else with_count<N - 1>(n, f);
+    }
+}
+
 template <int N> __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -777,26 +788,31 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 }
 
 // One 128-wide K stage of fp8 MFMAs for the direct-to-LDS fp8 kernel: the wavefront's WM x WN blocks of
-// 16 x 16 (and the W3 half for the up GEMM).  Same arithmetic as mma_stage's fp8 path, in a schedule that
-// keeps the register footprint fixed: B fragments of the stage stay in registers, A fragments and the
-// row scales are read one row block ahead; with more than 64 accumulator VGPRs a row block's MFMAs also
-// wait for the rescaling of the previous block's results, so only one block's MFMA results are live and
-// a 128 x 64 wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.  mid() runs once row
-// block MID_AT's MFMAs are issued: the kernel issues the second half of a ring refill there (the up GEMM
-// after its fourth row block, the down GEMM after its first; against the second for both: up 11.40 ->
-// 11.24 ms, down 5.88 -> 5.72 ms).
-template <bool UP, int WM, int WN, int BN, typename MID>
+// 16 x 16 (and the W3 half for the up GEMM), each the product of one 16-row weight fragment (first MFMA
+// operand) and one 16-row activation fragment (second), so a result holds [feature][token]: lane l has
+// features 4 (l / 16) + r, r = 0..3, of token l % 16.  All four values of a lane then share one row
+// scale, and the per-K-block rescale acc += p * (row scale * weight block scale) needs one scale product
+// per lane and row block (against four rows per lane in [token][feature] order: 2 instead of 8 multiplies
+// per four MFMAs).  B fragments of the stage stay in registers; A fragments and the row scale are read
+// one row block ahead.  With more than 64 accumulator VGPRs a row block's MFMAs also wait for the
+// rescaling of the previous block's results, so only one block's MFMA results are live and a 128 x 64
+// wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.  mid() runs once row block
+// MID_AT's MFMAs are issued (at the end when the wavefront computes fewer row blocks): the kernel issues
+// the second half of a ring refill there.  Only the first NB of the WM row blocks hold tile rows; the
+// others get no MFMAs, no rescale and no fragment reads (their accumulators stay zero, never stored).
+template <bool UP, int WM, int WN, int BN, int NB, typename MID>
 __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_lds, const float* sA_lds, float sb1,
                                        float sb3, int wm0, int wn0, int lane, f32x4 (&acc1)[WM][WN],
                                        f32x4 (&acc3)[WM][WN], MID&& mid)
 {
+    static_assert(NB >= 0 && NB <= WM, "row blocks");
     constexpr int MID_AT = UP ? 3 : 0;
     static_assert(WM > MID_AT, "mid() runs inside the row-block loop");
     const int r16 = lane & 15, q = lane >> 4;
     constexpr bool TIGHT = WM * WN * (UP ? 2 : 1) > 16;  // more than 64 accumulator VGPRs
     auto frag = [&](const uint8_t* base, int row) {
-        const i32x4 lo = *(const i32x4*)(base + swz(row, 2 * q));
-        const i32x4 hi = *(const i32x4*)(base + swz(row, 2 * q + 1));
+        const i32x4 lo = *(const i32x4*)(base + swzr<128>(row, 2 * q));
+        const i32x4 hi = *(const i32x4*)(base + swzr<128>(row, 2 * q + 1));
         return (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     };
     i32x8 b1[WN], b3[UP ? WN : 1];
@@ -805,11 +821,14 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
         b1[j] = frag(Bs_lds, wn0 + j * 16 + r16);
         if constexpr (UP) b3[j] = frag(Bs_lds, BN + wn0 + j * 16 + r16);
     }
-    // row scales of the lane's four rows 4q .. 4q + 3 of row block i (16-byte aligned)
-    auto scales = [&](int i) { return *(const f32x4*)(sA_lds + wm0 + i * 16 + 4 * q); };
+    auto scale = [&](int i) { return sA_lds[wm0 + i * 16 + r16]; };   // row scale of the lane's token
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (NB == 0) {
+        mid();
+        return;
+    }
     i32x8 a = frag(As_lds, wm0 + r16);
-    f32x4 sa = scales(0);
+    float sa = scale(0);
     if constexpr (TIGHT) {
         // Software pipeline over row blocks: block i's MFMAs are issued before block i - 1's results are
         // rescaled, so the matrix pipe runs while the vector ALU rescales.  Block i + 1's A operand
@@ -817,32 +836,32 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
         // two blocks' MFMA results are live.
         constexpr int NP = UP ? 2 * WN : WN;          // MFMA results per row block
         f32x4 pc[NP], pp[NP];
-        float p1s[4], p3s[4];                          // scale products of the previous block
+        float s1 = 0.f, s3 = 0.f;                      // scale products of the previous block
 #pragma unroll
-        for (int i = 0; i <= WM; i++) {
+        for (int i = 0; i <= NB; i++) {
             i32x8 a_next = a;
-            f32x4 sa_next = sa;
-            if (i < WM) {
+            float sa_next = sa;
+            if (i < NB) {
 #pragma unroll
                 for (int j = 0; j < WN; j++) {
-                    pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b1[j], zero, 0, 0, 0, 127, 0, 127);
+                    pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1[j], a, zero, 0, 0, 0, 127, 0, 127);
                     if constexpr (UP)
-                        pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
+                        pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b3[j], a, zero, 0, 0, 0, 127, 0, 127);
                 }
                 if (i == MID_AT) mid();
-                if (i + 1 < WM) {
+                if (i + 1 < NB) {
                     a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
-                    sa_next = scales(i + 1);
+                    sa_next = scale(i + 1);
                 }
             }
             if (i > 0) {
 #pragma unroll
                 for (int j = 0; j < WN; j++) {
 #pragma unroll
-                    for (int r = 0; r < 4; r++) acc1[i - 1][j][r] += pp[j][r] * p1s[r];
+                    for (int r = 0; r < 4; r++) acc1[i - 1][j][r] += pp[j][r] * s1;
                     if constexpr (UP) {
 #pragma unroll
-                        for (int r = 0; r < 4; r++) acc3[i - 1][j][r] += pp[WN + j][r] * p3s[r];
+                        for (int r = 0; r < 4; r++) acc3[i - 1][j][r] += pp[WN + j][r] * s3;
                     }
                 }
 #pragma unroll
@@ -851,48 +870,109 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                     else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i - 1][j]));
                 }
             }
-            if (i < WM) {
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    p1s[r] = sa[r] * sb1;
-                    p3s[r] = sa[r] * sb3;
-                }
+            if (i < NB) {
+                s1 = sa * sb1;
+                s3 = sa * sb3;
 #pragma unroll
                 for (int n = 0; n < NP; n++) pp[n] = pc[n];
                 a = a_next;
                 sa = sa_next;
             }
         }
+        if constexpr (NB <= MID_AT) mid();
         return;
     }
 #pragma unroll
-    for (int i = 0; i < WM; i++) {
+    for (int i = 0; i < NB; i++) {
         i32x8 a_next = a;
-        f32x4 sa_next = sa;
-        if (i + 1 < WM) {
+        float sa_next = sa;
+        if (i + 1 < NB) {
             a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
-            sa_next = scales(i + 1);
+            sa_next = scale(i + 1);
         }
-        float s1[4], s3[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            s1[r] = sa[r] * sb1;
-            s3[r] = sa[r] * sb3;
-        }
+        const float s1 = sa * sb1, s3 = sa * sb3;
 #pragma unroll
         for (int j = 0; j < WN; j++) {
-            const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b1[j], zero, 0, 0, 0, 127, 0, 127);
+            const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1[j], a, zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc1[i][j][r] += p1[r] * s1[r];
+            for (int r = 0; r < 4; r++) acc1[i][j][r] += p1[r] * s1;
             if constexpr (UP) {
-                const f32x4 p3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b3[j], zero, 0, 0, 0, 127, 0, 127);
+                const f32x4 p3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b3[j], a, zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * s3[r];
+                for (int r = 0; r < 4; r++) acc3[i][j][r] += p3[r] * s3;
             }
         }
         if (i == MID_AT) mid();
         a = a_next;
         sa = sa_next;
+    }
+    if constexpr (NB <= MID_AT) mid();
+}
+
+// Epilogue of the direct-to-LDS fp8 kernel, for the [feature][token] accumulator layout of mma_f8 (lane
+// l holds features 4 (l / 16) + r of token l % 16).  UP: h = round(silu(round g) * round u) through LDS
+// (BM x BN floats, each row's 16-byte chunks XOR-swizzled by token so a wavefront's 16 tokens write
+// distinct banks), then quantised per 1 x 128 group to E4M3 codes plus one scale per group.  Down: the
+// bf16 output tile through LDS (padded rows), then whole-line copies to the output rows.
+template <bool UP, int BM, int BN, int WM, int WN, int NT>
+__device__ __forceinline__ void f8_epilogue(const GemmArgs& g, uint8_t* smem, const f32x4 (&acc1)[WM][WN],
+                                            const f32x4 (&acc3)[WM][WN], int rows, int row0, int n0, int wm0,
+                                            int wn0, int tid)
+{
+    const int lane = tid & 63;
+    const int r16 = lane & 15, q = lane >> 4;
+    if constexpr (UP) {
+        static_assert(BN / 4 >= 16, "the chunk swizzle flips the low four bits of a row's chunk index");
+        float* hs = (float*)smem;                      // [BM][BN]; logical chunk c of row t at chunk c ^ (t % 16)
+#pragma unroll
+        for (int i = 0; i < WM; i++) {
+            const int t = wm0 + i * 16 + r16;
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                f32x4 v;
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    v[r] = round_bf16(silu_mul(round_bf16(acc1[i][j][r]), round_bf16(acc3[i][j][r])));
+                const int c = ((wn0 + j * 16) >> 2) + q;
+                *(f32x4*)(hs + t * BN + ((c ^ (t & 15)) << 2)) = v;
+            }
+        }
+        __syncthreads();
+        // 16 threads per (row, 128-column group), 8 columns (two chunks) each
+        constexpr int GROUPS = BM * (BN / 128);
+        for (int gi = tid >> 4; gi < GROUPS; gi += NT / 16) {
+            const int row = gi / (BN / 128), grp128 = gi % (BN / 128);
+            const int sub = tid & 15;
+            const int c0 = grp128 * 32 + 2 * sub;
+            const f32x4 va = *(const f32x4*)(hs + row * BN + ((c0 ^ (row & 15)) << 2));
+            const f32x4 vb = *(const f32x4*)(hs + row * BN + (((c0 + 1) ^ (row & 15)) << 2));
+            const float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+            float amax = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+            if (row < rows) {
+                uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
+                uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+                const int64_t orow = row0 + row;
+                *(uint2*)(g.out + orow * g.ldo + n0 + grp128 * 128 + sub * 8) = make_uint2(lo, hi);
+                if (sub == 0) g.outs[orow * g.ldos + (n0 + grp128 * 128) / 128] = sc;
+            }
+        }
+    } else {
+        constexpr int OSTR = BN * 2 + 16;              // padded LDS row of the bf16 output tile
+#pragma unroll
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                const uint32_t lo = (uint32_t)f32_to_bf16(acc1[i][j][0]) | ((uint32_t)f32_to_bf16(acc1[i][j][1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16(acc1[i][j][2]) | ((uint32_t)f32_to_bf16(acc1[i][j][3]) << 16);
+                *(uint2*)(smem + (wm0 + i * 16 + r16) * OSTR + (wn0 + j * 16 + 4 * q) * 2) = make_uint2(lo, hi);
+            }
+        __syncthreads();
+        store_tile_bf16<BM, BN, OSTR, NT>(smem, g.out, g.ldo, row0, rows, n0);
     }
 }
 
@@ -958,12 +1038,12 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
 
     // Per-lane source offsets, fixed over the K walk.  Load p of wavefront w fills LDS rows
     // (p * NW + w) * 8 .. + 8; lane l writes stored chunk l % 8 of row l / 8, which holds the logical chunk
-    // (l % 8) ^ (row % 8).
+    // stored there by swzr<128> (the row's swizzle repeats every 16 rows, so A and B rows share it).
     uint32_t off[PERW];
 #pragma unroll
     for (int p = 0; p < PERW; p++) {
         const int row = (p * NW + wave) * 8 + (lane >> 3);
-        const int lc = (lane & 7) ^ (row & 7);
+        const int lc = (swzr<128>(row, lane & 7) - row * 128) >> 4;
         if (p < PA) off[p] = (uint32_t)s_tok[row] * (uint32_t)g.lda + lc * 16;
         else if (p < PA + PB1) off[p] = (uint32_t)(n0 + row - BM) * (uint32_t)ldb + lc * 16;
         else off[p] = (uint32_t)(n0 + row - BM - BN) * (uint32_t)ldb + lc * 16;
@@ -996,6 +1076,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
         for (int j = 0; j < WN; j++) acc1[i][j] = acc3[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     const int cb = wn0 / 128;                          // the wavefront's weight block within the n-block
+    // 16-row blocks of this wavefront that hold tile rows (wave-uniform)
+    const int nrb = __builtin_amdgcn_readfirstlane(max(0, min(WM, (rows - wm0 + 15) / 16)));
 #pragma unroll
     for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1), 0, PERW, true);
     wait_vmcnt<(NSTG - 1) * NL>();
@@ -1004,40 +1086,31 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     // scales) from inside the next stage's MFMAs, so no wavefront stalls on a burst of loads before its
     // MFMAs (fp8 up GEMM 11.48 -> 11.19 ms with the second half after the second row block).  Every load
     // of the refill still precedes the next wait.
-    int buf = 0, pbuf = -1, pst = 0;
-    for (int s = 0; s < nstages; s++) {
-        const float* sc = scl[buf];
-        const uint8_t* st = ring + buf * STAGE;
-        mma_f8<UP, WM, WN, BN>(st, st + BM * 128, sc, sc[BM + cb], UP ? sc[BM + 64 + cb] : 0.f, wm0, wn0, lane, acc1,
-                               acc3, [&] { if (pbuf >= 0) issue(pbuf, pst, PERW / 2, PERW, true); });
-        pbuf = -1;
-        if (s + 1 < nstages) {
-            wait_vmcnt<(NSTG - 2) * NL>();             // stage s + 1 has landed
-            lds_barrier();                             // ... for every wavefront; stage s is read
-            pst = min(s + NSTG, nstages - 1);          // past the end: the last stage again (never read)
-            issue(buf, pst, 0, PERW / 2, false);
-            pbuf = buf;
-            buf = buf + 1 == NSTG ? 0 : buf + 1;
+    // The K walk for NB computed row blocks (a compile-time count, so the MFMA / rescale pipeline of mma_f8
+    // stays one straight-line schedule; the walk is instantiated per count, like the bf16 kernel's).
+    auto k_walk = [&](auto nb_tag) {
+        constexpr int NB = decltype(nb_tag)::value;
+        int buf = 0, pbuf = -1, pst = 0;
+        for (int s = 0; s < nstages; s++) {
+            const float* sc = scl[buf];
+            const uint8_t* st = ring + buf * STAGE;
+            mma_f8<UP, WM, WN, BN, NB>(st, st + BM * 128, sc, sc[BM + cb], UP ? sc[BM + 64 + cb] : 0.f, wm0, wn0, lane,
+                                       acc1, acc3, [&] { if (pbuf >= 0) issue(pbuf, pst, PERW / 2, PERW, true); });
+            pbuf = -1;
+            if (s + 1 < nstages) {
+                wait_vmcnt<(NSTG - 2) * NL>();         // stage s + 1 has landed
+                lds_barrier();                         // ... for every wavefront; stage s is read
+                pst = min(s + NSTG, nstages - 1);      // past the end: the last stage again (never read)
+                issue(buf, pst, 0, PERW / 2, false);
+                pbuf = buf;
+                buf = buf + 1 == NSTG ? 0 : buf + 1;
+            }
         }
-    }
+    };
+    with_count<WM>(nrb, k_walk);
     wait_vmcnt<0>();                                   // no load may still target this block's LDS
     lds_barrier();
-    if constexpr (UP) {
-        gemm_epilogue<ET_FP8, UP, true, BM, BN, WM, WN, NT>(g, ring, acc1, acc3, rows, row0, n0, wm0, wn0, tid);
-    } else {
-        // bf16 output rows through LDS (16x16 layout: lane holds rows 4 (lane / 16) + r, column lane % 16)
-        const int r16 = lane & 15, q = lane >> 4;
-#pragma unroll
-        for (int i = 0; i < WM; i++)
-#pragma unroll
-            for (int j = 0; j < WN; j++)
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    *(uint16_t*)(ring + (wm0 + i * 16 + 4 * q + r) * OSTR + (wn0 + j * 16 + r16) * 2) =
-                        f32_to_bf16(acc1[i][j][r]);
-        __syncthreads();
-        store_tile_bf16<BM, BN, OSTR, NT>(ring, g.out, g.ldo, row0, rows, n0);
-    }
+    f8_epilogue<UP, BM, BN, WM, WN, NT>(g, ring, acc1, acc3, rows, row0, n0, wm0, wn0, tid);
 }
 
 // fp8 activation quantisation of x: per row, per 128-column group, s = amax / 448 (1 if amax = 0),

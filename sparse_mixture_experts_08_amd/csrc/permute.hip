@@ -22,7 +22,7 @@ constexpr int kFusedMaxTokens = 256;
 
 // Tile list for groups with counts cnt[0..E) and offsets off[0..E]: shared expert (group E, rows
 // [T*k, T*k + T)) first when `shared` is set, then the experts of [g0, g1) ascending, each cut into
-// bm-row tiles.  One thread per expert; called by all NT threads of the block.
+// ceil(rows / bm) tiles of at most bm rows.  One thread per expert; called by all NT threads of the block.
 template <int NT>
 __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int k, int bm, TileRange tr, int4* tiles,
                             int32_t* ntiles, int* scan_lds)
@@ -36,7 +36,14 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int k,
         const int nt = (c + bm - 1) / bm;
         int total;
         const int base = carry + block_exclusive_scan<NT>(nt, &total, scan_lds);
-        for (int r = 0, i = 0; r < c; r += bm, i++) tiles[base + i] = make_int4(e, off[e] + r, min(bm, c - r), 0);
+        // The expert's ceil(c / 16) blocks of 16 rows dealt evenly over its nt = ceil(c / bm) tiles (tile i
+        // takes blocks [i nb / nt, (i + 1) nb / nt), 1 to bm rows, only the last one ragged), so an expert
+        // just over a multiple of bm rows gets no nearly empty last tile.
+        const int nb = (c + 15) / 16;
+        for (int i = 0; i < nt; i++) {
+            const int r0 = 16 * (int)((int64_t)i * nb / nt), r1 = min(16 * (int)((int64_t)(i + 1) * nb / nt), c);
+            tiles[base + i] = make_int4(e, off[e] + r0, r1 - r0, 0);
+        }
         carry += total;
     }
     if (threadIdx.x == 0) ntiles[0] = carry;
