@@ -32,7 +32,9 @@ from sparse_mixture_experts_08_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {W.BF16: 2500.0, W.FP8_E4M3: 5000.0, W.F32: 157.3}
-FP32_VALU_PEAK_TFLOPS = 157.3  # 256 CUs x 2.4 GHz x 256 fp32 flops/clock (packed FMA counted)
+# fp32 vector peak without packed FMA (this build emits none): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 78.6
+PROBE_LIB = os.path.join(ROOT, "sparse_mixture_experts_08_amd", "libmoe_probe.so")
 
 
 class HipEvents:
@@ -61,6 +63,64 @@ class HipEvents:
     def close(self):
         for i in range(len(self.arr)):
             self.hip.hipEventDestroy(self.arr[i])
+
+
+def measured_peaks(dev, read_gib=16, reps=3):
+    """What this GPU sustains, as the measured denominators of the roofline fractions: a streaming read of
+    read_gib GiB (far beyond the 256 MB last-level cache) with libmoe_probe.so's read kernel; back-to-back
+    bf16 and fp8 MFMAs (eight independent chains per wavefront, two wavefronts per SIMD) with its MFMA
+    kernel; and a large dense bf16 GEMM through torch.matmul (the vendor library).  Best of `reps` runs."""
+    L = ctypes.CDLL(PROBE_LIB)
+    L.moe_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    L.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    nbytes = read_gib << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    grid = 256 * 16
+
+    def read():
+        if L.moe_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, grid, ctypes.c_void_p(sink.data_ptr()),
+                                   stream):
+            raise RuntimeError("moe_probe_stream_read failed")
+    read()
+    out["hbm_read_GBs"] = max(nbytes / (event_ms(read, 1) * 1e-3) / 1e9 for _ in range(reps))
+    del buf
+    torch.cuda.empty_cache()
+    flops = ctypes.c_double()
+    for name, dt in (("mfma_bf16_TFLOPs", 1), ("mfma_fp8_TFLOPs", 2)):
+        def mfma():
+            if L.moe_probe_mfma(dt, 20000, 512, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops), stream):
+                raise RuntimeError("moe_probe_mfma failed")
+        mfma()
+        out[name] = max(flops.value / (event_ms(mfma, 1) * 1e-3) / 1e12 for _ in range(reps))
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    torch.matmul(a, b, out=c)
+    out["gemm_bf16_TFLOPs"] = max(2.0 * 8192 ** 3 / (event_ms(lambda: torch.matmul(a, b, out=c), 5) * 1e-3) / 1e12
+                                  for _ in range(reps))
+    del a, b, c
+    torch.cuda.empty_cache()
+    out["how"] = (f"streaming read of {read_gib} GiB ({grid} blocks of 256 threads, 16-byte loads); 2048 wavefronts "
+                  "x 8 chains of back-to-back v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_16x16x128_f8f6f4; "
+                  "torch.matmul bf16 8192^3; best of 3")
+    return out
+
+
+def with_measured(roof, peaks, w_dtype):
+    """Adds the fraction against the measured ceiling of the roofline's bound to a roofline dict."""
+    if peaks is None:
+        return roof
+    key = {"hbm": "hbm_read_GBs", "mfma": {W.BF16: "mfma_bf16_TFLOPs", W.FP8_E4M3: "mfma_fp8_TFLOPs"}.get(w_dtype)}
+    k = key.get(roof["bound"])
+    if k:
+        roof["peak_measured"] = peaks[k]
+        roof["frac_measured"] = roof["achieved"] / peaks[k]
+    return roof
 
 
 def algorithmic(wl, counts, e0=0, e1=None, n_shared=None):
@@ -132,7 +192,8 @@ def cpu_baseline(wl, inp, max_tokens, shard=None, min_seconds=10.0):
         t_fwd += time.perf_counter() - t0
         passes += 1
     per_token = t_route / wl.T + t_fwd / (n * passes)
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "omp_threads": O.num_threads(), "kind": "oracle",
             "sample": f"routing of all {wl.T} tokens ({t_route:.2f} s) + experts and combine of {n} tokens, "
                       f"{passes} passes ({t_fwd:.2f} s); tokens/s = 1 / (route s/token + expert s/token)"}
 
@@ -243,6 +304,8 @@ def run_layer(wl, inp, args, dev):
     roof["traffic"] = measured_traffic(wl.name if shard is None else f"{wl.name}/shard-ep8", "up_gemm")
     # keep the documented key order: bound, achieved, peak, unit, frac, traffic
     roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel", "kernel_ms")}
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    roof = with_measured(roof, peaks, wl.w_dtype)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -261,6 +324,7 @@ def run_layer(wl, inp, args, dev):
     if shard is not None:
         out["config"]["parallelism"] = f"ep8 rank {args.rank} (one GPU's share)"
     out["roofline"] = roof
+    out["peaks_measured"] = peaks
     out["layer"] = {"algorithmic_GB": alg["layer_bytes"] / 1e9, "touched_experts": alg["touched"],
                     "GB_per_s": alg["layer_bytes"] / (ms_per_step * 1e-3) / 1e9,
                     "hbm_frac": alg["layer_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -307,7 +371,8 @@ def run_route_limited(wl, inp, args, dev):
         t0 = time.perf_counter()
         O.route_limited(h["x"], h["Wg"], W.to_numpy(inp.get("bias")), allowed.numpy(), wl.k, wl.act_dtype)
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": wl.T / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+        out["cpu_baseline"] = {"value": wl.T / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "omp_threads": O.num_threads(), "kind": "oracle",
                                "sample": f"route_limited of all {wl.T} tokens ({dt:.2f} s)"}
     return out
 
@@ -356,6 +421,7 @@ def main():
     ap.add_argument("--rank", type=int, default=0, choices=range(8), help="expert-parallel rank / device (of 8)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring the GPU's sustained HBM / MFMA ceilings")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of the oracle baseline (about)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

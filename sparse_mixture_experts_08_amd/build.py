@@ -1,4 +1,5 @@
-"""Build libmoe.so (the HIP kernels and the C ABI of include/moe.h) in-tree for gfx950 with hipcc."""
+"""Build libmoe.so (the HIP kernels and the C ABI of include/moe.h) and libmoe_probe.so (the benchmark's
+measurement kernels of include/moe_probe.h) in-tree for gfx950 with hipcc."""
 import hashlib
 import os
 import re
@@ -12,6 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["moe_abi.hip", "router.hip", "permute.hip", "gemm.hip", "combine.hip"]
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
+PROBE_SOURCES = ["peak_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 vector ops are switched off for all device code.
@@ -44,15 +47,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+def _link(objs, lib, verbose):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,109 @@
+// peak_probe.hip -- measurement kernels for the denominators of the roofline fractions: the HBM read rate
+// a plain streaming kernel reaches, and the MFMA rate back-to-back matrix instructions reach, on the GPU
+// at hand (the published 8 TB/s and 2.5 / 5.0 PFLOP/s are peaks at the nominal clock; these are what the
+// chip sustains).  Not part of the layer: libmoe_probe.so, used by the benchmark only.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_probe.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Every thread reads 16-byte vectors, four in flight per iteration, grid-stride over the buffer, and folds
+// them into an xor; the fold is stored only when it equals a value no finite buffer of ones produces, so
+// the loads cannot be removed and nothing is written in practice.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, uint64_t n16, uint32_t* sink)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    uint32_t acc = 0;
+    uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+// CHAINS independent accumulators per wavefront, each advanced by one MFMA per iteration: the matrix pipe
+// never waits on a result.  Operands are lane values that cannot be folded at compile time.
+template <int CHAINS>
+__global__ __launch_bounds__(256) void mfma_bf16_kernel(int iters, float* sink)
+{
+    const float s = (float)(threadIdx.x & 7) * 0.125f;
+    bf16x8 a, b;
+    for (int e = 0; e < 8; e++) {
+        a[e] = (__bf16)(s + e);
+        b[e] = (__bf16)(s - e);
+    }
+    f32x16 acc[CHAINS];
+    for (int c = 0; c < CHAINS; c++) acc[c] = (f32x16){};
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+        for (int c = 0; c < CHAINS; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < CHAINS; c++) asm volatile("" : "+a"(acc[c]));   // keeps every chain in its registers
+    }
+    float t = 0.f;
+    for (int c = 0; c < CHAINS; c++)
+        for (int e = 0; e < 16; e++) t += acc[c][e];
+    if (t == 1.2345f) sink[blockIdx.x] = t;
+}
+
+template <int CHAINS>
+__global__ __launch_bounds__(256) void mfma_fp8_kernel(int iters, float* sink)
+{
+    const int s = (int)(threadIdx.x & 7);
+    i32x8 a, b;
+    for (int e = 0; e < 8; e++) {
+        a[e] = 0x38383838 + s + e;
+        b[e] = 0x30303030 + s - e;
+    }
+    f32x4 acc[CHAINS];
+    for (int c = 0; c < CHAINS; c++) acc[c] = (f32x4){};
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+        for (int c = 0; c < CHAINS; c++)
+            acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[c], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int c = 0; c < CHAINS; c++) asm volatile("" : "+a"(acc[c]));   // keeps every chain in its registers
+    }
+    float t = 0.f;
+    for (int c = 0; c < CHAINS; c++)
+        for (int e = 0; e < 4; e++) t += acc[c][e];
+    if (t == 1.2345f) sink[blockIdx.x] = t;
+}
+
+}  // namespace
+
+extern "C" int moe_probe_stream_read(const void* buf, size_t bytes, unsigned grid, uint32_t* sink, hipStream_t stream)
+{
+    if (!buf || !sink || bytes < 16 || ((uintptr_t)buf & 15) || grid == 0) return 1;
+    stream_read_kernel<<<grid, 256, 0, stream>>>((const uint4*)buf, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int moe_probe_mfma(int dtype, int iters, unsigned grid, float* sink, double* flops, hipStream_t stream)
+{
+    if (!sink || !flops || iters <= 0 || grid == 0) return 1;
+    constexpr int CHAINS = 8;
+    const double waves = (double)grid * 4;
+    if (dtype == 1) {
+        mfma_bf16_kernel<CHAINS><<<grid, 256, 0, stream>>>(iters, sink);
+        *flops = waves * iters * CHAINS * (2.0 * 32 * 32 * 16);
+    } else if (dtype == 2) {
+        mfma_fp8_kernel<CHAINS><<<grid, 256, 0, stream>>>(iters, sink);
+        *flops = waves * iters * CHAINS * (2.0 * 16 * 16 * 128);
+    } else {
+        return 2;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}

@@ -38,6 +38,14 @@ def test_bench_json_line():
         assert key in roof, key
     assert roof["bound"] in ("hbm", "mfma", "alu") and roof["peak"] > 0 and roof["achieved"] > 0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) <= 1e-6 * max(1.0, roof["frac"])
+    pk = r["peaks_measured"]
+    for key in ("hbm_read_GBs", "mfma_bf16_TFLOPs", "mfma_fp8_TFLOPs", "gemm_bf16_TFLOPs"):
+        assert pk[key] > 0, key
+    # the sustained ceilings lie below the published peaks (8 TB/s; 2.5 / 5.0 PFLOP/s at the nominal clock)
+    assert pk["hbm_read_GBs"] <= 8000 * 1.02 and pk["mfma_bf16_TFLOPs"] <= 2500 * 1.02
+    assert pk["mfma_fp8_TFLOPs"] <= 5000 * 1.02
+    if "peak_measured" in roof:
+        assert abs(roof["frac_measured"] - roof["achieved"] / roof["peak_measured"]) <= 1e-6 * max(1.0, roof["frac_measured"])
     cb = r["cpu_baseline"]
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cb, key
