@@ -22,6 +22,9 @@
  *  - Argument errors are detected on the host before any launch; nothing is written then.
  *    Launch failures return MOE_ERR_HIP.  Device faults surface at the caller's next synchronisation.
  *  - Calls are reentrant.  Concurrent calls must use different workspaces and outputs.
+ *  - fp8 weights are quantised in 128 x 128 blocks and fp8 activations in 1 x 128 groups: the block
+ *    edge is fixed at 128 (the configurations' quantisation block), so d, inter and inter_shared are
+ *    multiples of 128 for every dtype.
  *  - Inputs are assumed finite; NaN/Inf inputs are outside the contract.
  */
 #ifndef MOE_H
@@ -77,9 +80,16 @@ size_t moe_workspace_size(const moe_shape_t* shape);
 
 /*
  * Routing only: router logits, top-k, softmax and the expert-sorted permutation.
+ * Gate: "DeepSeek-V3's mixture-of-experts architecture explained", "The architecture in one diagram",
+ * block pseudocode (router_logits = self.gate(x); weights, indices = topk(router_logits, k=8); weights =
+ * softmax(weights)); counts and the expert-sorted rows: "DeepSeek-V3.2-Exp / Mixture of experts", MoE
+ * forward excerpt (bincount of the indices; torch.where(indices == i) per expert, row-major).
  *   x            [T, d] act_dtype
  *   Wg           [E, d] fp32 router weight, the gate's nn.Linear(d, E) weight (logits = x Wg^T);
- *                16-byte aligned
+ *                16-byte aligned.  This is the transpose of the math-orientation [d, E] ("Wg 7168 x 256"
+ *                in the configurations): the nn.Linear [out, in] layout the pages' gate wraps, which
+ *                gives every expert's FMA chain one contiguous row.  A [d, E] array is passed as its
+ *                transpose.
  *   bias         [E] fp32 logit bias added before selection, or NULL
  *   idx    out   [T, k] int32 selected experts, descending logit, ties -> lower expert index
  *   w      out   [T, k] fp32 softmax over the k selected logits
@@ -96,6 +106,10 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const float* Wg,
 
 /*
  * The whole layer: routing, routed SwiGLU experts, shared SwiGLU expert and the weighted combine.
+ * "DeepSeek-V3.2-Exp / Mixture of experts / Shared expert": MoE forward excerpt (y = zeros in fp32;
+ * y[idx] += expert(x[idx]) * weights[idx, top] per expert; y += shared_experts(x)), "All 5 steps" and the
+ * MLP forward excerpt (w2(silu(w1(x)) * w3(x)), silu * mul in fp32, cast back before w2); routing as in
+ * moe_route.
  *   x        [T, d] act_dtype (not modified; must not alias y)
  *   Wg, bias as in moe_route
  *   W1, W3   [E, inter, d] w_dtype (nn.Linear [out, in] layout: g = x W1^T per expert)
