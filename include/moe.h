@@ -16,7 +16,8 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by the caller.  The
- *    library allocates and frees nothing and keeps no state between calls.
+ *    library allocates and frees nothing and keeps no state between calls, except moe_forward_noalloc's
+ *    static device scratch (see there).
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream) without any host
  *    synchronisation; results are valid once the caller synchronises the stream.
  *  - Argument errors are detected on the host before any launch; nothing is written then.
@@ -44,7 +45,8 @@ typedef enum {
     MOE_ERR_INVALID_ARG = 1,   /* null required pointer, negative size, k > E, y aliasing x, bad alignment */
     MOE_ERR_UNSUPPORTED = 2,   /* dtype combination, d / inter not multiples of 128, k > 16, E > 1024 */
     MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_size() */
-    MOE_ERR_HIP = 4            /* a kernel launch failed */
+    MOE_ERR_HIP = 4,           /* a kernel launch failed */
+    MOE_ERR_SCRATCH = 5        /* moe_forward_noalloc: the shape needs more than MOE_NOALLOC_SCRATCH_BYTES */
 } moe_status_t;
 
 typedef enum {
@@ -217,6 +219,31 @@ moe_status_t moe_forward_shard(const moe_shape_t* shape, const void* x, const fl
  */
 moe_status_t moe_expert_utilization(int64_t E, const int32_t* counts, float* util, int32_t* flags,
                                     int32_t* summary, hipStream_t stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments, results and guarantees as
+ * moe_forward, without the workspace arguments.  Its workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library: each GPU the library runs on holds one copy from the
+ * moment the library's kernels are loaded on it until the process ends (64 MiB; enough for moe_forward's
+ * workspace at decode sizes, e.g. T <= 256 tokens at d = 7168, E = 256, k = 8, inter = 2048).
+ *  - A shape whose moe_workspace_size() exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH
+ *    before any device work.  Argument errors as moe_forward.
+ *  - The call allocates and frees nothing.  Its first call on a device looks up the array's device
+ *    address there (hipGetSymbolAddress); failure returns MOE_ERR_HIP.
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last call's contents (no call reads
+ *    what an earlier one left: nothing in it needs clearing).  Calls that overlap on one GPU -- on
+ *    different streams, or from different host threads without ordering -- race on it: serialise them,
+ *    or use moe_forward with a workspace per concurrent call.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_noalloc(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
+                                 const void* W1, const void* W3, const void* W2,
+                                 const float* W1s, const float* W3s, const float* W2s,
+                                 const void* S1, const void* S3, const void* S2,
+                                 const float* S1s, const float* S3s, const float* S2s,
+                                 void* y, int32_t* idx_out, float* w_out, int32_t* counts_out,
+                                 hipStream_t stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t status);

@@ -12,9 +12,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP",
+          5: "MOE_ERR_SCRATCH"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_staged", "moe_route_limited",
-           "moe_forward_shard", "moe_expert_utilization", "moe_status_string")
+           "moe_forward_shard", "moe_expert_utilization", "moe_forward_noalloc", "moe_status_string")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 NUM_STAGES = 7
 STAGE_NAMES = ("router_logits", "topk_softmax", "permute", "x_quant", "up_gemm", "down_gemm", "combine")
 
@@ -57,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_shard.argtypes = [sp] + [vp] * 4 + [i64] * 3 + [vp] * 17 + [ctypes.c_size_t, vp, vp]
         L.moe_expert_utilization.restype = ctypes.c_int
         L.moe_expert_utilization.argtypes = [i64] + [vp] * 5
+        L.moe_forward_noalloc.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [sp] + [vp] * 19 + [vp]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         _LIB = L
@@ -169,6 +173,37 @@ def moe_forward(x, Wg, bias, W1, W3, W2, S1, S3, S2, k, scales=None, y=None, wor
     if st:
         raise MoeError(st, "moe_forward")
     return (y, r) if routing else y
+
+
+def moe_forward_noalloc(x, Wg, bias, W1, W3, W2, S1, S3, S2, k, scales=None, y=None, routing=False):
+    """moe_forward_noalloc: moe_forward with the library's static device scratch as its workspace (nothing is
+    allocated by the call itself; y and the routing copies are allocated here unless given)."""
+    T, d = x.shape
+    E, inter = W1.shape[0], W1.shape[1]
+    shape = make_shape(T, d, E, k, inter, S1.shape[0], _act_code(x), _w_code(W1))
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    sc = scales or {}
+    r = None
+    if routing:
+        r = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+                 w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                 counts=torch.empty(E, dtype=torch.int32, device=dev))
+    st = lib().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(W1), _ptr(W3), _ptr(W2),
+                                   _ptr(sc.get("W1s")), _ptr(sc.get("W3s")), _ptr(sc.get("W2s")), _ptr(S1), _ptr(S3),
+                                   _ptr(S2), _ptr(sc.get("S1s")), _ptr(sc.get("S3s")), _ptr(sc.get("S2s")), _ptr(y),
+                                   _ptr(r and r["idx"]), _ptr(r and r["w"]), _ptr(r and r["counts"]), _stream(dev))
+    if st:
+        raise MoeError(st, "moe_forward_noalloc")
+    return (y, r) if routing else y
+
+
+def forward_inputs_noalloc(inp: dict, k: int, **kw):
+    """moe_forward_noalloc over a dict produced by workloads.generate (device tensors)."""
+    scales = {n: inp[n] for n in ("W1s", "W3s", "W2s", "S1s", "S3s", "S2s") if inp.get(n) is not None}
+    return moe_forward_noalloc(inp["x"], inp["Wg"], inp.get("bias"), inp["W1"], inp["W3"], inp["W2"], inp["S1"],
+                               inp["S3"], inp["S2"], k, scales=scales or None, **kw)
 
 
 def forward_inputs(inp: dict, k: int, **kw):

@@ -3,6 +3,8 @@
 // grouped down GEMM -> combine), all enqueued on the caller's stream with no host synchronisation.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -113,6 +115,7 @@ extern "C" const char* moe_status_string(moe_status_t st)
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP launch failure";
+    case MOE_ERR_SCRATCH: return "shape needs more workspace than the static scratch of moe_forward_noalloc holds";
     }
     return "unknown status";
 }
@@ -168,6 +171,32 @@ extern "C" moe_status_t moe_route_limited(const moe_shape_t* shape, const void* 
                       workspace_bytes, stream);
 }
 
+// Host-side checks of a layer call (everything but the workspace), shared by the entry points.
+static moe_status_t check_layer_args(const moe_shape_t* shape, const void* x, const float* Wg, int64_t e0, int64_t e1,
+                                     int64_t n_shared, const void* W1, const void* W3, const void* W2,
+                                     const float* W1s, const float* W3s, const float* W2s, const void* S1,
+                                     const void* S3, const void* S2, const float* S1s, const float* S3s,
+                                     const float* S2s, const void* out)
+{
+    moe_status_t st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape_t& s = *shape;
+    if (e0 < 0 || e1 > s.E || e0 > e1 || n_shared < 0 || n_shared > s.inter_shared) return MOE_ERR_INVALID_ARG;
+    if (n_shared % 128) return MOE_ERR_UNSUPPORTED;
+    if (s.T == 0) return MOE_OK;
+    const bool routed = e1 > e0, with_shared = n_shared > 0;
+    const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
+    if (!x || !Wg || !out) return MOE_ERR_INVALID_ARG;
+    if (routed && (!W1 || !W3 || !W2 || (fp8 && (!W1s || !W3s || !W2s)))) return MOE_ERR_INVALID_ARG;
+    if (with_shared && (!S1 || !S3 || !S2 || (fp8 && (!S1s || !S3s || !S2s)))) return MOE_ERR_INVALID_ARG;
+    if (x == out) return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, Wg, out, routed ? W1 : x, routed ? W3 : x, routed ? W2 : x, with_shared ? S1 : x,
+                          with_shared ? S3 : x, with_shared ? S2 : x};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
 // The layer or one expert-parallel rank's share of it.  Routed experts [e0, e1) (weights of expert e at
 // index e - e0 of W1/W3/W2), n_shared shared hidden features; y (act dtype, rounded) or y_partial (fp32).
 static moe_status_t layer_impl(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
@@ -178,23 +207,15 @@ static moe_status_t layer_impl(const moe_shape_t* shape, const void* x, const fl
                                float* w_out, int32_t* counts_out, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t* events)
 {
-    moe_status_t st = check_shape(shape);
+    void* out = y ? y : (void*)y_partial;
+    moe_status_t st = check_layer_args(shape, x, Wg, e0, e1, n_shared, W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s,
+                                       S3s, S2s, out);
     if (st != MOE_OK) return st;
     const moe_shape_t& s = *shape;
-    if (e0 < 0 || e1 > s.E || e0 > e1 || n_shared < 0 || n_shared > s.inter_shared) return MOE_ERR_INVALID_ARG;
-    if (n_shared % 128) return MOE_ERR_UNSUPPORTED;
     if (s.T == 0) return MOE_OK;
-    const bool routed = e1 > e0, with_shared = n_shared > 0;
+    const bool with_shared = n_shared > 0;
     const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
-    void* out = y ? y : (void*)y_partial;
-    if (!x || !Wg || !out || !workspace) return MOE_ERR_INVALID_ARG;
-    if (routed && (!W1 || !W3 || !W2 || (fp8 && (!W1s || !W3s || !W2s)))) return MOE_ERR_INVALID_ARG;
-    if (with_shared && (!S1 || !S3 || !S2 || (fp8 && (!S1s || !S3s || !S2s)))) return MOE_ERR_INVALID_ARG;
-    if (x == out) return MOE_ERR_INVALID_ARG;
-    const void* ptrs[] = {x, Wg, out, routed ? W1 : x, routed ? W3 : x, routed ? W2 : x, with_shared ? S1 : x,
-                          with_shared ? S3 : x, with_shared ? S2 : x};
-    for (const void* p : ptrs)
-        if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+    if (!workspace) return MOE_ERR_INVALID_ARG;
     Workspace ws = carve_workspace(s, workspace);
     if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
 
@@ -274,4 +295,65 @@ extern "C" moe_status_t moe_expert_utilization(int64_t E, const int32_t* counts,
     if (E <= 0 || E > (1 << 30) || !counts || !util || !flags || !summary) return MOE_ERR_INVALID_ARG;
     MOE_TRY(launch_expert_utilization((int)E, counts, util, flags, summary, stream));
     return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------------
+// moe_forward without a workspace argument, for callers that cannot allocate device memory.  The
+// workspace is this file-scope device array: every GPU the library runs on holds its own copy, from the
+// loading of the library's code object on that GPU until the process ends.  In host code `scratch` names
+// a host-side stand-in, not device memory, so its device address is looked up once per device (with that
+// device current) and only that address is handed to the kernels.
+// ---------------------------------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int NOALLOC_MAX_DEVICES = 64;
+
+// Device address of `scratch` on the current device (looked up on the first call per device), or null
+// with *err set.
+static void* scratch_on_current_device(hipError_t* err)
+{
+    static std::mutex mu;
+    static void* addr[NOALLOC_MAX_DEVICES] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *err = e;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+extern "C" moe_status_t moe_forward_noalloc(const moe_shape_t* shape, const void* x, const float* Wg,
+                                            const float* bias, const void* W1, const void* W3, const void* W2,
+                                            const float* W1s, const float* W3s, const float* W2s, const void* S1,
+                                            const void* S3, const void* S2, const float* S1s, const float* S3s,
+                                            const float* S2s, void* y, int32_t* idx_out, float* w_out,
+                                            int32_t* counts_out, hipStream_t stream)
+{
+    if (!shape) return MOE_ERR_INVALID_ARG;
+    moe_status_t st = check_layer_args(shape, x, Wg, 0, shape->E, shape->inter_shared, W1, W3, W2, W1s, W3s, W2s,
+                                       S1, S3, S2, S1s, S3s, S2s, y);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return MOE_OK;
+    if (carve_workspace(*shape, nullptr).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    hipError_t err = hipSuccess;
+    void* ws = scratch_on_current_device(&err);
+    if (!ws) return MOE_ERR_HIP;
+    return layer_impl(shape, x, Wg, bias, nullptr, 0, shape->E, shape->inter_shared, W1, W3, W2, W1s, W3s, W2s, S1,
+                      S3, S2, S1s, S3s, S2s, y, nullptr, idx_out, w_out, counts_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                      stream, nullptr);
 }

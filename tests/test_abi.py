@@ -107,9 +107,41 @@ def test_empty_input_is_a_no_op():
 
 
 def test_status_strings():
-    for st in range(5):
+    for st in range(6):
         assert B.moe_status_string(st)
     assert "workspace" in B.moe_status_string(3)
+    assert "scratch" in B.moe_status_string(5)
+
+
+def _call_noalloc(shape, ptrs=None):
+    # x, Wg, bias, W1, W3, W2, W1s, W3s, W2s, S1, S3, S2, S1s, S3s, S2s, y, idx, w, counts
+    L = B.lib()
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(19)] if ptrs is None else ptrs
+    return L.moe_forward_noalloc(ctypes.byref(shape), *p, None)
+
+
+def test_noalloc_host_side_errors():
+    # Everything the no-allocation entry point refuses is refused on the host, before its first device call
+    # (the lookup of its static scratch): shapes, pointers, and shapes whose workspace exceeds the scratch.
+    assert B.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert _call_noalloc(_shape(k=9, E=8)) == 1
+    assert _call_noalloc(_shape(d=7100)) == 2
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(19)]
+    p[0] = None                                          # x
+    assert _call_noalloc(_shape(), p) == 1
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(19)]
+    p[15] = p[0]                                         # y aliasing x
+    assert _call_noalloc(_shape(), p) == 1
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(19)]
+    p[6] = None                                          # fp8 W1s
+    assert _call_noalloc(_shape(w_dtype=B.MOE_FP8_E4M3), p) == 1
+    # the decode configuration fits the 64 MiB scratch, a prefill-sized one does not
+    assert B.moe_workspace_size(_shape(T=64)) <= B.NOALLOC_SCRATCH_BYTES
+    assert B.moe_workspace_size(_shape(T=256)) <= B.NOALLOC_SCRATCH_BYTES
+    assert B.moe_workspace_size(_shape(T=512)) > B.NOALLOC_SCRATCH_BYTES
+    assert _call_noalloc(_shape(T=512)) == 5
+    assert _call_noalloc(_shape(T=4096)) == 5
+    assert _call_noalloc(_shape(T=0), [None] * 19) == 0
 
 
 def _call_shard(shape, e0, e1, n_shared, ptrs=None, ws_bytes=1 << 30):
