@@ -577,7 +577,7 @@ __device__ __forceinline__ void store_tile_bf16(const uint8_t* tile, uint8_t* ou
 // shorten it.  Fewer staged bytes per MFMA did, which is why the block tile is as large as the register
 // file allows.
 // ---------------------------------------------------------------------------------------------------
-template <bool UP, int BM, int RB, int NSTG, int NW>
+template <bool UP, int BM, int RB, int NA, int NBS, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 {
     constexpr int WAVES_M = BM / 128, WAVES_N = NW / WAVES_M;
@@ -586,21 +586,25 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
     constexpr int BN = WAVES_N * WCOL;                  // block columns (per half for UP)
     constexpr int NB = UP ? 2 * BN : BN;               // B rows per stage
     constexpr int ROWS = BM + NB;
-    constexpr int STAGE = ROWS * RB;
+    constexpr int ASTAGE = BM * RB, BSTAGE = NB * RB;  // one stage of A rows / of weight rows
     constexpr int CPR = RB / 16, RPL = 64 / CPR;       // 16-byte chunks per row, rows per 1-KB load
     constexpr int PERW = ROWS / RPL / NW;              // 1-KB loads per wavefront per stage
     constexpr int PA = BM / RPL / NW, PB1 = BN / RPL / NW; // ... of which A rows, W1 (or W2) rows
+    constexpr int PBW = PERW - PA;                     // ... of which weight rows
     constexpr int KS = RB / 32;                        // 16-element K steps per stage
     static_assert(BM == 128 || BM == 256, "128- or 256-row tiles");
     static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
-    static_assert(ROWS % (NW * RPL) == 0 && BM % (NW * RPL) == 0 && BN % (NW * RPL) == 0 && (NSTG - 1) * PERW < 64,
-                  "whole loads per wavefront, vmcnt range");
+    static_assert(NA >= 2 && NBS >= NA, "the weight ring is at least as deep as the A ring");
+    static_assert(ROWS % (NW * RPL) == 0 && BM % (NW * RPL) == 0 && BN % (NW * RPL) == 0 &&
+                  (NA - 1) * PA + (NBS - 1) * PBW < 64, "whole loads per wavefront, vmcnt range");
     static_assert(NJ >= 1, "at least one 32-column block per wavefront");
-    static_assert(BM * 4 <= STAGE, "row table fits the first stage buffer");
+    static_assert(BM * 4 <= ASTAGE, "row table fits the first stage buffer");
 
     constexpr int OSTR = BN * 2 + 16;                  // epilogue: padded LDS row of the block's output tile
-    constexpr int RING = NSTG * STAGE > BM * OSTR ? NSTG * STAGE : BM * OSTR;
+    constexpr int RINGS = NA * ASTAGE + NBS * BSTAGE;
+    constexpr int RING = RINGS > BM * OSTR ? RINGS : BM * OSTR;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
+    uint8_t* const ringB = ring + NA * ASTAGE;         // the weight rows' ring follows the A rows' ring
     int* s_tok = (int*)ring;                           // row table, dead before the first load into the ring
 
     int tile, nb;
@@ -643,19 +647,23 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
     // K stages walked from a start rotated by the n-block (as in grouped_gemm_kernel), in a fixed order.
     const int nstages = K / (RB / 2);
     const int kshift = (nb * g.krot) % nstages;
-    const uint32_t ring0 = lds_addr(ring);
-    // Stage s into ring buffer buf: this wavefront's loads p0 .. p1 - 1.
-    auto issue = [&](int buf, int s, int p0, int p1) {
-        const int ks = s + kshift >= nstages ? s + kshift - nstages : s + kshift;
-        const int64_t koff = (int64_t)ks * RB;
-        const uint8_t* a = g.A + koff;
+    const uint32_t ringA0 = lds_addr(ring), ringB0 = lds_addr(ringB);
+    auto kstage = [&](int s) { return (int64_t)(s + kshift >= nstages ? s + kshift - nstages : s + kshift) * RB; };
+    // The A rows of stage s into A buffer buf: this wavefront's loads 0 .. PA - 1.
+    auto issue_a = [&](int buf, int s) {
+        const uint8_t* a = g.A + kstage(s);
+        const uint32_t dst = ringA0 + buf * ASTAGE + wave * 1024;
+#pragma unroll
+        for (int p = 0; p < PA; p++) dma16(a, off[p], dst + p * NW * 1024);
+    };
+    // The weight rows of stage s into weight buffer buf: this wavefront's loads PA .. PERW - 1.
+    auto issue_b = [&](int buf, int s) {
+        const int64_t koff = kstage(s);
         const uint8_t* b1 = W1 + koff;
         const uint8_t* b3 = W3 + koff;
-        const uint32_t dst = ring0 + buf * STAGE + wave * 1024;
+        const uint32_t dst = ringB0 + buf * BSTAGE + wave * 1024;
 #pragma unroll
-        for (int p = p0; p < p1; p++) {
-            dma16(p < PA ? a : p < PA + PB1 ? b1 : b3, off[p], dst + p * NW * 1024);
-        }
+        for (int p = PA; p < PERW; p++) dma16(p < PA + PB1 ? b1 : b3, off[p], dst + (p - PA) * NW * 1024);
     };
 
     f32x16 acc1[4][NJ], acc3[4][UP ? NJ : 1];
@@ -678,16 +686,19 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
         constexpr int NRB = decltype(nrb_tag)::value;
         constexpr int NF = NRB == 0 ? 0 : NRB + (UP ? 2 * NJ : NJ);   // fragment reads per K step
         constexpr int NM = NRB * (UP ? 2 * NJ : NJ);                   // MFMAs per K step
-        auto read = [&](int buf, int kk, Frags& f) {
+        // (The row swizzle repeats every 16 rows, so a weight row keeps it without the BM offset it has in
+        // the load offsets above.)
+        auto read = [&](int abuf, int bbuf, int kk, Frags& f) {
             if constexpr (NRB > 0) {
-                const uint8_t* st = ring + buf * STAGE;
+                const uint8_t* sa = ring + abuf * ASTAGE;
+                const uint8_t* sb = ringB + bbuf * BSTAGE;
                 const int ch = 2 * kk + kh;
 #pragma unroll
-                for (int i = 0; i < NRB; i++) f.a[i] = *(const bf16x8*)(st + swzr<RB>(wm0 + 32 * i + r32, ch));
+                for (int i = 0; i < NRB; i++) f.a[i] = *(const bf16x8*)(sa + swzr<RB>(wm0 + 32 * i + r32, ch));
 #pragma unroll
                 for (int j = 0; j < NJ; j++) {
-                    f.b1[j] = *(const bf16x8*)(st + swzr<RB>(BM + wn0 + 32 * j + r32, ch));
-                    if constexpr (UP) f.b3[j] = *(const bf16x8*)(st + swzr<RB>(BM + BN + wn0 + 32 * j + r32, ch));
+                    f.b1[j] = *(const bf16x8*)(sb + swzr<RB>(wn0 + 32 * j + r32, ch));
+                    if constexpr (UP) f.b3[j] = *(const bf16x8*)(sb + swzr<RB>(BN + wn0 + 32 * j + r32, ch));
                 }
             }
         };
@@ -702,8 +713,8 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
                 }
         };
         // One K step: the fragments of the next step are read (one read after each of the first NF MFMAs).
-        auto kstep = [&](const Frags& cur, int buf_next, int kk_next, Frags& nxt) {
-            read(buf_next, kk_next, nxt);
+        auto kstep = [&](const Frags& cur, int abuf_next, int bbuf_next, int kk_next, Frags& nxt) {
+            read(abuf_next, bbuf_next, kk_next, nxt);
             mma(cur);
 #pragma unroll
             for (int m = 0; m < NM; m++) {
@@ -712,49 +723,54 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
             }
         };
 
-        // Ring: stage t lives in buffer t % NSTG.  The prologue loads stages 0 .. NSTG - 1; at the end of
-        // stage s (all its fragments read) stage s + 1 is awaited and published, and stage s's buffer is
-        // refilled with stage s + NSTG (past the end: the last stage again, into a buffer nobody reads), so
-        // NSTG - 1 stages are in flight while one is computed and every wait is the same vmcnt.
-        // A freed buffer is refilled around the K step that follows the barrier: the up GEMM issues half of
-        // the stage's loads before that step and half after it (prefill up GEMM 3.44 -> 3.415 ms, within
-        // run-to-run spread), the down GEMM all of them before it (split, its skewed time grows by 1 %).
-        auto refill = [&](int b, int st, auto&& step) {
-            issue(b, st, 0, UP ? PERW / 2 : PERW);
+        // Rings: stage t's A rows live in A buffer t % NA and its weight rows in weight buffer t % NBS.  The
+        // prologue loads the A rows of stages 0 .. NA - 1 and the weight rows of stages 0 .. NBS - 1; at the
+        // end of stage s (all its fragments read) stage s + 1 is awaited and published, and stage s's
+        // buffers are refilled with the A rows of stage s + NA and the weight rows of stage s + NBS (past the
+        // end: the last stage again, into buffers nobody reads).  Weight rows, which stream from HBM or the
+        // last-level cache, thus have NBS - 1 stages of lead, A rows (L2 hits mostly) NA - 1.  Loads are issued
+        // in the order A(s + NA), weights(s + NBS), so every wait for stage s + 1 is the same vmcnt: only the
+        // weight loads issued after it (PBW per wavefront) may remain in flight.
+        // The refill sits around the K step that follows the barrier: the A rows before it, the weight rows
+        // after it for the up GEMM (before it for the down GEMM).
+        auto refill = [&](int ab, int bb, int s, auto&& step) {
+            issue_a(ab, min(s + NA, nstages - 1));
+            if constexpr (!UP) issue_b(bb, min(s + NBS, nstages - 1));
             step();
-            if constexpr (UP) issue(b, st, PERW / 2, PERW);
+            if constexpr (UP) issue_b(bb, min(s + NBS, nstages - 1));
         };
 #pragma unroll
-        for (int t = 0; t < NSTG; t++) issue(t, min(t, nstages - 1), 0, PERW);
-        wait_vmcnt<(NSTG - 1) * PERW>();               // stage 0 only, its successors stay in flight
+        for (int t = 0; t < NBS; t++) {
+            if (t < NA) issue_a(t, min(t, nstages - 1));
+            issue_b(t, min(t, nstages - 1));
+        }
+        wait_vmcnt<(NA - 1) * PA + (NBS - 1) * PBW>(); // stage 0 only, its successors stay in flight
         lds_barrier();
         Frags f0, f1;
-        read(0, 0, f0);
-        int buf = 0;
+        read(0, 0, 0, f0);
+        int ab = 0, bb = 0;
         for (int s = 0; s + 1 < nstages; s++) {
-            const int nbuf = buf + 1 == NSTG ? 0 : buf + 1;
+            const int nab = ab + 1 == NA ? 0 : ab + 1, nbb = bb + 1 == NBS ? 0 : bb + 1;
             if constexpr (KS == 4) {
-                kstep(f0, buf, 1, f1);
-                kstep(f1, buf, 2, f0);
-                kstep(f0, buf, 3, f1);
-                wait_vmcnt<(NSTG - 2) * PERW>();
-                lds_barrier();
-                refill(buf, min(s + NSTG, nstages - 1), [&] { kstep(f1, nbuf, 0, f0); });
+                kstep(f0, ab, bb, 1, f1);
+                kstep(f1, ab, bb, 2, f0);
+                kstep(f0, ab, bb, 3, f1);
             } else {
-                kstep(f0, buf, 1, f1);
-                wait_vmcnt<(NSTG - 2) * PERW>();
-                lds_barrier();
-                refill(buf, min(s + NSTG, nstages - 1), [&] { kstep(f1, nbuf, 0, f0); });
+                kstep(f0, ab, bb, 1, f1);
             }
-            buf = nbuf;
+            wait_vmcnt<PBW>();
+            lds_barrier();
+            refill(ab, bb, s, [&] { kstep(f1, nab, nbb, 0, f0); });
+            ab = nab;
+            bb = nbb;
         }
         if constexpr (KS == 4) {
-            kstep(f0, buf, 1, f1);
-            kstep(f1, buf, 2, f0);
-            kstep(f0, buf, 3, f1);
+            kstep(f0, ab, bb, 1, f1);
+            kstep(f1, ab, bb, 2, f0);
+            kstep(f0, ab, bb, 3, f1);
             mma(f1);
         } else {
-            kstep(f0, buf, 1, f1);
+            kstep(f0, ab, bb, 1, f1);
             mma(f1);
         }
     };
@@ -1174,7 +1190,7 @@ template <bool UP>
 static void launch_w(GemmArgs a, hipStream_t stream)
 {
     const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
-    grouped_gemm_w_kernel<UP, 256, 128, 2, 8><<<(unsigned)nblk, 512, 0, stream>>>(a);
+    grouped_gemm_w_kernel<UP, 256, 128, 2, 3, 8><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
 
 // fp8 tiles of 128 or 256 rows: a ring of three stages for 128-row tiles, two for 256 (LDS).
