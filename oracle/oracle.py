@@ -25,9 +25,12 @@ class OracleShape(ctypes.Structure):
 def lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        path = os.environ.get("MOE_ORACLE_LIB")   # another build of the same source (the sanitizer build)
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.oracle_round_bf16_from_double.restype = ctypes.c_float
         L.oracle_round_bf16_from_double.argtypes = [ctypes.c_double]
