@@ -864,7 +864,7 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                     if constexpr (UP)
                         pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b3[j], a, zero, 0, 0, 0, 127, 0, 127);
                 }
-                if (i == MID_AT) mid();
+                if (UP && i == MID_AT) mid();
                 if (i + 1 < NB) {
                     a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
                     sa_next = scale(i + 1);
@@ -880,12 +880,26 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                         for (int r = 0; r < 4; r++) acc3[i - 1][j][r] += pp[WN + j][r] * s3;
                     }
                 }
+                if (!UP && i < NB) {
+                    // Down GEMM: after each MFMA of block i, four of block i - 1's rescale FMAs (and block
+                    // i + 1's fragment reads after the first), so the vector ALU works while the matrix
+                    // pipe runs instead of both wavefronts of a SIMD rescaling at once with the pipe idle.
+                    // The up GEMM, with twice the MFMAs per block, ran slower under the same grouping and
+                    // keeps the compiler's order.
+#pragma unroll
+                    for (int m = 0; m < NP; m++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (m == 0) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < WN; j++) {
                     if constexpr (UP) asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i - 1][j]), "v"(acc3[i - 1][j]));
                     else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i - 1][j]));
                 }
             }
+            if (!UP && i < NB && i == MID_AT) mid();
             if (i < NB) {
                 s1 = sa * sb1;
                 s3 = sa * sb3;
