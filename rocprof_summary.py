@@ -1,6 +1,12 @@
 """Summarise the rocprofv3 runs of one bench.py workload into profiles/.
 
 python rocprof_summary.py WORKLOAD VARIANT TRACE_DIR FETCH_DIR WRITE_DIR [CLOCK_DIR]
+python rocprof_summary.py counters WORKLOAD PASS_DIR [PASS_DIR ...]
+
+The second form writes profiles/counters_<workload>.md from `rocprofv3 --pmc ...` runs of the grouped GEMM
+kernels (one directory per counter pass): per kernel the counters averaged over its dispatches and the
+derived figures (MFMA busy, VALU busy, LDS busy and bank-conflict stalls, L2 hit rate and read latency,
+wavefront wait share).
 
 TRACE_DIR holds the CSV output of `rocprofv3 --kernel-trace --stats -f csv -o run`, FETCH_DIR and WRITE_DIR
 that of `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` over a bench.py run that ends with one plain
@@ -65,7 +71,74 @@ def gemm_role(kernel):
     return "up_gemm" if up == "true" else "down_gemm"
 
 
+# Counter passes of the GEMM profiles (each within one pass's per-block limits: <= 8 SQ, <= 4 TCC, <= 4 TCP).
+COUNTER_PASSES = [
+    "MfmaUtil VALUBusy LdsUtil LDSBankConflict GRBM_COUNT",
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_LDS SQ_INSTS_LDS SQ_INSTS_VALU "
+    "SQ_INSTS_MFMA",
+    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum TCP_PENDING_STALL_CYCLES_sum "
+    "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_TOTAL_CACHE_ACCESSES_sum GRBM_GUI_ACTIVE",
+]
+
+
+def counters_main(workload, dirs):
+    vals = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        for r in _csv(d, "counter_collection.csv"):
+            if "moe::" in r["Kernel_Name"]:
+                vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    avg = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    lines = [f"# rocprofv3 counters of the grouped GEMMs: {workload}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp on an MI355X; R = repository root, OUT = an output "
+             "directory; one run per counter pass):", "", "```"]
+    bench = f"python3 $R/bench.py --workload {workload} --steps 1 --warmup 1 --no-cpu-baseline --no-peaks"
+    for i, p in enumerate(COUNTER_PASSES):
+        lines.append(f'rocprofv3 --pmc {p} --kernel-include-regex "grouped_gemm" -f csv -d $OUT/p{i + 1} -o run -- '
+                     f"{bench}")
+    lines.append(f"python3 $R/rocprof_summary.py counters {workload} " +
+                 " ".join(f"$OUT/p{i + 1}" for i in range(len(COUNTER_PASSES))))
+    lines += ["```", "", "Derived figures (per dispatch, averaged over dispatches):", "",
+              "- MFMA busy, VALU busy, LDS busy, LDS bank-conflict stall: rocprofv3's MfmaUtil, VALUBusy, LdsUtil "
+              "and LDSBankConflict (percent of the kernel's active cycles);",
+              "- L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS); L2 read latency = TCP_TCC_READ_REQ_LATENCY / "
+              "TCP_TCC_READ_REQ (cycles per request, as the L1 sees it);",
+              "- wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wavefront cycles waiting on a dependency: "
+              "memory, LDS or a barrier); VALU / MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA (SQ_INSTS_VALU "
+              "counts the MFMAs too).", "",
+              "| kernel | MFMA busy % | VALU busy % | LDS busy % | LDS conflict stall % | L2 hit % | L2 read "
+              "latency | wait share % | VALU / MFMA |", "|---|---|---|---|---|---|---|---|---|"]
+
+    def g(c, k):
+        return avg[k].get(c)
+
+    def fmt(v, f="{:.1f}"):
+        return "–" if v is None else f.format(v)
+    for k in sorted(avg, key=lambda k: -(g("GRBM_GUI_ACTIVE", k) or 0)):
+        hit, miss = g("TCC_HIT_sum", k), g("TCC_MISS_sum", k)
+        lat, req = g("TCP_TCC_READ_REQ_LATENCY_sum", k), g("TCP_TCC_READ_REQ_sum", k)
+        wait, wc = g("SQ_WAIT_INST_ANY", k), g("SQ_WAVE_CYCLES", k)
+        iv, im = g("SQ_INSTS_VALU", k), g("SQ_INSTS_MFMA", k)
+        lines.append(f"| `{k}` | {fmt(g('MfmaUtil', k))} | {fmt(g('VALUBusy', k))} | {fmt(g('LdsUtil', k))} | "
+                     f"{fmt(g('LDSBankConflict', k), '{:.2f}')} | "
+                     f"{fmt(None if hit is None or miss is None else 100 * hit / max(hit + miss, 1))} | "
+                     f"{fmt(None if lat is None or not req else lat / req, '{:.0f}')} | "
+                     f"{fmt(None if wait is None or not wc else 100 * wait / wc)} | "
+                     f"{fmt(None if iv is None or not im else iv / im, '{:.2f}')} |")
+    lines += ["", "Raw counter values (average per dispatch):", "", "| kernel | counter | value |", "|---|---|---|"]
+    for k in sorted(avg):
+        for c in sorted(avg[k]):
+            lines.append(f"| `{k}` | {c} | {avg[k][c]:.4g} |")
+    lines += ["", "GEMM code fingerprint when measured (sha256[:16] of csrc/gemm.hip without comments or whitespace): "
+              f"`{code_fingerprint(GEMM_SRC)}`", ""]
+    name = f"counters_{workload}.md"
+    open(os.path.join(ROOT, "profiles", name), "w").write("\n".join(lines))
+    print(f"wrote profiles/{name}")
+
+
 def main():
+    if sys.argv[1] == "counters":
+        counters_main(sys.argv[2], sys.argv[3:])
+        return
     workload, variant, trace_dir, fetch_dir, write_dir = sys.argv[1:6]
     clock_dir = sys.argv[6] if len(sys.argv) > 6 else None
     key = workload if variant == "layer" else f"{workload}/{variant}"
@@ -85,14 +158,14 @@ def main():
     v = f" --variant {variant}"
     bench = f"python3 $R/bench.py --workload {workload}{v}"
     lines.append(f"rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace -o run -- {bench} "
-                 "--steps 10 --warmup 2 --no-cpu-baseline")
+                 "--steps 10 --warmup 2 --no-cpu-baseline --no-peaks")
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         lines.append(f'rocprofv3 --pmc {c} --kernel-include-regex "moe::|copyBuffer" -f csv -d '
-                     f"$OUT/{c} -o run -- {bench} --steps 1 --warmup 1 --no-cpu-baseline "
+                     f"$OUT/{c} -o run -- {bench} --steps 1 --warmup 1 --no-cpu-baseline --no-peaks "
                      "--copy-calibration-mib 1024")
     if clock_dir:
         lines.append(f'rocprofv3 --pmc GRBM_COUNT --kernel-include-regex "moe::" -f csv -d $OUT/GRBM_COUNT -o run '
-                     f"-- {bench} --steps 2 --warmup 1 --no-cpu-baseline")
+                     f"-- {bench} --steps 2 --warmup 1 --no-cpu-baseline --no-peaks")
     lines.append(f"python3 $R/rocprof_summary.py {workload} {variant} $OUT/trace $OUT/FETCH_SIZE $OUT/WRITE_SIZE"
                  + (" $OUT/GRBM_COUNT" if clock_dir else ""))
     lines += ["```", "", "## Kernel durations (--kernel-trace --stats; every dispatch in the run, including the "
