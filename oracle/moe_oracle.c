@@ -178,6 +178,58 @@ static void topk_one(const float* L, int64_t E, int64_t k, int32_t* idx)
     }
 }
 
+/*
+ * Group-limited top-k ["Technical Architecture and Core Innovations", "Architectural Breakthroughs", item 1,
+ * "Hierarchical Dynamic Routing": tokens are first distributed over 8 expert groups by a softmax, then 2
+ * experts per group are selected].  Reading (the one under which 2 experts per group agree with top-k):
+ * the E experts form G groups of E / G consecutive experts; a group's candidates are its two best
+ * experts (ranks_above); its score is the fp32 sum of their two logits; the k / 2 groups with the largest
+ * scores are kept (a softmax over the group scores keeps their order), equal scores ordered by ascending
+ * group index; the token's k experts are the kept groups' pairs, listed in rank order.
+ */
+static void topk_grouped_one(const float* L, int64_t E, int64_t k, int64_t G, int32_t* idx)
+{
+    const int64_t gs = E / G, keep = k / 2;
+    int64_t first[64], second[64];
+    float score[64];
+    int kept[64];
+    for (int64_t g = 0; g < G; g++) {
+        int64_t a = -1, b = -1;
+        for (int64_t e = g * gs; e < (g + 1) * gs; e++) {
+            if (a < 0 || ranks_above(L, e, a)) {
+                b = a;
+                a = e;
+            } else if (b < 0 || ranks_above(L, e, b)) {
+                b = e;
+            }
+        }
+        first[g] = a;
+        second[g] = b;
+        score[g] = L[a] + L[b];                                  /* one fp32 add */
+        kept[g] = 0;
+    }
+    for (int64_t r = 0; r < keep; r++) {
+        int64_t best = -1;
+        for (int64_t g = 0; g < G; g++)
+            if (!kept[g] && (best < 0 || score[g] > score[best])) best = g;   /* ties: the lower group */
+        kept[best] = 1;
+    }
+    /* the kept pairs in rank order, by repeatedly taking the best remaining candidate */
+    for (int64_t j = 0; j < k; j++) {
+        int64_t best = -1;
+        for (int64_t g = 0; g < G; g++) {
+            if (!kept[g]) continue;
+            const int64_t cand[2] = {first[g], second[g]};
+            for (int c = 0; c < 2; c++) {
+                int taken = 0;
+                for (int64_t jj = 0; jj < j; jj++) taken |= (idx[jj] == cand[c]);
+                if (!taken && (best < 0 || ranks_above(L, cand[c], best))) best = cand[c];
+            }
+        }
+        idx[j] = (int32_t)best;
+    }
+}
+
 /* Softmax over the k selected logits (fp64 from the fp32 logits; the max is the first one). */
 static void softmax_selected(const float* L, const int32_t* idx, int64_t k, float* w)
 {
@@ -199,10 +251,14 @@ static void softmax_selected(const float* L, const int32_t* idx, int64_t k, floa
  * Any output pointer may be NULL except idx and w.
  */
 static int route_impl(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype, const void* x,
-                      const float* Wg, const float* bias, const uint8_t* allowed, float* logits_out, int32_t* idx,
-                      float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos)
+                      const float* Wg, const float* bias, const uint8_t* allowed, int64_t n_group, float* logits_out,
+                      int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                      int32_t* pos)
 {
     if (k < 1 || k > E || k > 64) return 1;
+    /* group-limited: G groups of at least two experts, k even, k / 2 groups kept */
+    if (n_group && (n_group < 1 || n_group > 64 || E % n_group || E / n_group < 2 || k % 2 || k / 2 > n_group))
+        return 1;
     if (allowed) {   /* at least one allowed expert; with fewer than k, the rest come at -inf, weight 0 */
         int64_t n_allowed = 0;
         for (int64_t e = 0; e < E; e++) n_allowed += allowed[e] != 0;
@@ -219,7 +275,8 @@ static int route_impl(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype,
             for (int64_t e = 0; e < E; e++) L[t * E + e] = L[t * E + e] + (allowed[e] ? 0.0f : -INFINITY);
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; t++) {
-        topk_one(L + t * E, E, k, idx + t * k);
+        if (n_group) topk_grouped_one(L + t * E, E, k, n_group, idx + t * k);
+        else topk_one(L + t * E, E, k, idx + t * k);
         softmax_selected(L + t * E, idx + t * k, k, w + t * k);
     }
     if (!logits_out) free(L);
@@ -251,8 +308,18 @@ int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int act_dtype, cons
                  const float* Wg, const float* bias, float* logits_out, int32_t* idx, float* w,
                  int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos)
 {
-    return route_impl(T, d, E, k, act_dtype, x, Wg, bias, NULL, logits_out, idx, w, counts, offsets, sorted_slots,
-                      pos);
+    return route_impl(T, d, E, k, act_dtype, x, Wg, bias, NULL, 0, logits_out, idx, w, counts, offsets,
+                      sorted_slots, pos);
+}
+
+/* Group-limited routing (topk_grouped_one) over n_group groups. */
+int oracle_route_grouped(int64_t T, int64_t d, int64_t E, int64_t k, int64_t n_group, int act_dtype, const void* x,
+                         const float* Wg, const float* bias, float* logits_out, int32_t* idx, float* w,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos)
+{
+    if (n_group < 1) return 1;
+    return route_impl(T, d, E, k, act_dtype, x, Wg, bias, NULL, n_group, logits_out, idx, w, counts, offsets,
+                      sorted_slots, pos);
 }
 
 /* Routing restricted to the experts with allowed[e] != 0 (at least one of them). */
@@ -261,7 +328,7 @@ int oracle_route_limited(int64_t T, int64_t d, int64_t E, int64_t k, int act_dty
                          int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                          int32_t* pos)
 {
-    return route_impl(T, d, E, k, act_dtype, x, Wg, bias, allowed, logits_out, idx, w, counts, offsets,
+    return route_impl(T, d, E, k, act_dtype, x, Wg, bias, allowed, 0, logits_out, idx, w, counts, offsets,
                       sorted_slots, pos);
 }
 

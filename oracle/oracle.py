@@ -44,6 +44,7 @@ def lib():
         L.oracle_forward.argtypes = [ctypes.POINTER(OracleShape)] + [vp] * 15 + [i64, vp, vp, vp]
         L.oracle_swiglu_rows.argtypes = [ctypes.POINTER(OracleShape)] + [vp] * 6 + [i64, i64, vp, vp]
         L.oracle_route_limited.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_route_grouped.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_expert_utilization.argtypes = [i64, vp, vp, vp, vp]
         L.oracle_forward_shard.argtypes = [ctypes.POINTER(OracleShape)] + [vp] * 15 + [i64, i64, i64, i64, i64, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
@@ -133,6 +134,26 @@ def route_limited(x: np.ndarray, Wg: np.ndarray, bias, allowed: np.ndarray, k: i
                                     _p(out["sorted_slots"]), _p(out["pos"]))
     if rc:
         raise ValueError(f"oracle_route_limited failed ({rc})")
+    return out
+
+
+def route_grouped(x: np.ndarray, Wg: np.ndarray, bias, k: int, n_group: int, act_dtype: int) -> dict:
+    """route() with group-limited selection: the k / 2 groups (of n_group) with the largest sums of their
+    two best logits, two experts from each."""
+    x = np.ascontiguousarray(x)
+    Wg = np.ascontiguousarray(Wg, dtype=np.float32)
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    T, d = x.shape
+    E = Wg.shape[0]
+    out = dict(logits=np.empty((T, E), np.float32), idx=np.empty((T, k), np.int32),
+               w=np.empty((T, k), np.float32), counts=np.empty(E, np.int32),
+               offsets=np.empty(E + 1, np.int32), sorted_slots=np.empty(T * k, np.int32),
+               pos=np.empty(T * k, np.int32))
+    rc = lib().oracle_route_grouped(T, d, E, k, n_group, act_dtype, _p(x), _p(Wg), _p(bias), _p(out["logits"]),
+                                    _p(out["idx"]), _p(out["w"]), _p(out["counts"]), _p(out["offsets"]),
+                                    _p(out["sorted_slots"]), _p(out["pos"]))
+    if rc:
+        raise ValueError(f"oracle_route_grouped failed ({rc})")
     return out
 
 

@@ -148,3 +148,105 @@ def test_shard_expert_range_is_weighted_expert_sum(oracle):
                 ye = (F.silu(X[t] @ inp["W1"][e].double().T) * (X[t] @ inp["W3"][e].double().T)) @ inp["W2"][e].double().T
                 ref[t] += float(r["w"][t, j]) * ye.numpy()
     assert np.allclose(part, ref, rtol=1e-5, atol=1e-6)
+
+
+# --- group-limited ("hierarchical") routing ------------------------------------------------------
+# "Technical Architecture and Core Innovations", "Architectural Breakthroughs", item 1: tokens are
+# distributed over 8 expert groups by a softmax, then 2 experts per group are selected.  Reading: the
+# k / 2 groups with the largest sums of their two best logits are kept, two experts from each.
+
+def _route_logits_grouped(oracle, L, k, n_group):
+    """Oracle grouped routing of given fp32 logits L [T, E]: token t's row of x is one-hot at t, so its
+    logits are exactly column t of Wg (the chain of a single nonzero term adds that term to +0)."""
+    T, E = L.shape
+    x = np.eye(T, max(T, 8), dtype=np.float32)
+    Wg = np.zeros((E, x.shape[1]), np.float32)
+    Wg[:, :T] = L.T
+    r = oracle.route_grouped(x, Wg, None, k, n_group, F32)
+    assert np.array_equal(r["logits"], L.astype(np.float32))
+    return r
+
+
+def _best_selection_by_enumeration(l, k, n_group):
+    """Brute force: among every choice of k / 2 groups and two experts in each, the selection with the
+    largest total logit (exact sum of the fp32 values), returned with the runner-up's total."""
+    E = len(l)
+    gs = E // n_group
+    groups = [list(range(g * gs, (g + 1) * gs)) for g in range(n_group)]
+    totals = []
+    for gsel in itertools.combinations(range(n_group), k // 2):
+        pair_choices = [list(itertools.combinations(groups[g], 2)) for g in gsel]
+        for pairs in itertools.product(*pair_choices):
+            sel = tuple(sorted(e for p in pairs for e in p))
+            totals.append((sum(Fraction(float(l[e])) for e in sel), sel))
+    totals.sort(key=lambda v: v[0], reverse=True)
+    return totals[0][1], totals[0][0], totals[1][0]
+
+
+@pytest.mark.parametrize("E,G,k", [(12, 4, 4), (16, 8, 6), (16, 4, 8), (18, 3, 6), (10, 5, 2)])
+def test_grouped_routing_maximises_total_logit_over_two_per_group_selections(oracle, E, G, k):
+    # Two experts from each of k / 2 groups with the largest total logit: that is the kept groups' best
+    # pairs, whatever the order the groups are compared in.  Random logits, so the maximum is unique.
+    g = torch.Generator().manual_seed(E * 100 + G * 10 + k)
+    L = torch.randn(40, E, generator=g).numpy()
+    r = _route_logits_grouped(oracle, L, k, G)
+    for t in range(L.shape[0]):
+        sel, best, second = _best_selection_by_enumeration(L[t], k, G)
+        assert best > second                                   # a unique maximum (no near-tie here)
+        assert tuple(sorted(r["idx"][t].tolist())) == sel, t
+
+
+def test_grouped_routing_slot_order_pairs_and_weights(oracle):
+    g = torch.Generator().manual_seed(5)
+    T, E, G, k = 60, 32, 8, 8
+    L = torch.randn(T, E, generator=g).numpy()
+    r = _route_logits_grouped(oracle, L, k, G)
+    for t in range(T):
+        idx = r["idx"][t]
+        lt = L[t][idx]
+        assert (np.diff(lt) <= 0).all()                        # descending logit (slot order of top-k)
+        grp = idx // (E // G)
+        vals, cnt = np.unique(grp, return_counts=True)
+        assert len(vals) == k // 2 and (cnt == 2).all()        # exactly two experts from k / 2 groups
+        for gg in vals:                                        # ... each group's two best
+            row = L[t, gg * (E // G):(gg + 1) * (E // G)]
+            assert sorted(idx[grp == gg].tolist()) == sorted((np.argsort(-row, kind="stable")[:2] + gg * (E // G)).tolist())
+        ref = torch.softmax(torch.from_numpy(lt).double(), 0).float().numpy()   # softmax over the k selected
+        assert np.abs(r["w"][t] - ref).max() <= 1e-7
+    c = np.bincount(r["idx"].ravel(), minlength=E)
+    assert np.array_equal(r["counts"], c) and r["offsets"][-1] == T * k
+
+
+def test_grouped_routing_special_cases(oracle):
+    g = torch.Generator().manual_seed(6)
+    x, Wg = _bf16(torch.randn(50, 64, generator=g)), torch.randn(16, 64, generator=g).numpy()
+    # one group and k = 2: the two best experts overall, i.e. plain top-2 routing
+    a, b = oracle.route_grouped(x, Wg, None, 2, 1, BF16), oracle.route(x, Wg, None, 2, BF16)
+    for key in ("idx", "w", "counts", "offsets", "sorted_slots", "pos"):
+        assert np.array_equal(a[key], b[key]), key
+    # groups of two experts and k = E: every expert, in plain top-E order
+    a, b = oracle.route_grouped(x, Wg, None, 16, 8, BF16), oracle.route(x, Wg, None, 16, BF16)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["w"], b["w"])
+    # groups of two experts: kept groups are those with the largest pair sums (fp32 adds), ties to the
+    # lower group; small integer logits make sums exact and ties frequent
+    L = torch.randint(-3, 4, (80, 12), generator=g).float().numpy()
+    r = _route_logits_grouped(oracle, L, 4, 6)
+    for t in range(L.shape[0]):
+        s = L[t].reshape(6, 2).sum(1)
+        order = sorted(range(6), key=lambda gg: (-s[gg], gg))
+        assert sorted(set((r["idx"][t] // 2).tolist())) == sorted(order[:2]), t
+    # ties inside a group go to the lower expert index; a +1e4 bias on one group's experts keeps it
+    L = np.zeros((3, 16), np.float32)
+    r = _route_logits_grouped(oracle, L, 4, 4)
+    assert (r["idx"] == np.array([0, 1, 4, 5])).all()
+    L = torch.randn(20, 16, generator=g).numpy()
+    L[:, 12:16] += 1e4
+    r = _route_logits_grouped(oracle, L, 4, 4)
+    assert ((r["idx"] // 4) == 3).sum(1).tolist() == [2] * 20
+
+
+def test_grouped_routing_rejects_inconsistent_shapes(oracle):
+    x, Wg = np.zeros((4, 8), np.float32), np.zeros((16, 8), np.float32)
+    for k, G in ((3, 4), (4, 3), (10, 4), (4, 16), (4, 0)):      # odd k, G not dividing E, k / 2 > G, 1 per group
+        with pytest.raises(ValueError):
+            oracle.route_grouped(x, Wg, None, k, G, F32)
