@@ -11,6 +11,7 @@ around it on the launch stream, over the timed steps) and the CPU oracle timed o
   shard-ep8      moe_forward_shard of one of 8 expert-parallel ranks (E/8 experts, 1/8 of the shared
                  expert's features; the all-reduce over ranks is not part of it)
   route-limited  moe_route_limited with the experts of one of 8 devices allowed
+  route-grouped  moe_route_grouped: two experts from each of the k / 2 best of 8 expert groups
   utilization    moe_expert_utilization over the workload's expert counts
 """
 import argparse
@@ -34,6 +35,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {W.BF16: 2500.0, W.FP8_E4M3: 5000.0, W.F32: 157.3}
 # fp32 vector peak without packed FMA (this build emits none): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
 FP32_VALU_PEAK_TFLOPS = 78.6
+# the router's logit kernel: fp32 FMA chains on the vector ALU up to this many tokens, fp32 MFMA above
+ROUTER_FEW_MAX_T = 512
 PROBE_LIB = os.path.join(ROOT, "sparse_mixture_experts_08_amd", "libmoe_probe.so")
 
 
@@ -337,43 +340,57 @@ def run_layer(wl, inp, args, dev):
     return out
 
 
-def run_route_limited(wl, inp, args, dev):
-    # the experts of device `rank` of 8 (contiguous blocks of E/8), as a device_expert_map would list them
+def run_route(wl, inp, args, dev, grouped):
+    """Routing alone: device-limited (the experts of device `rank` of 8, contiguous blocks of E/8, as a
+    device_expert_map would list them) or group-limited (8 groups, two experts from each of k / 2)."""
     ne = max(wl.E // 8, wl.k)
     allowed = torch.zeros(wl.E, dtype=torch.uint8)
     allowed[args.rank * ne:(args.rank + 1) * ne] = 1
     a_dev = allowed.to(dev)
+    n_group = 8
     shape = B.make_shape(wl.T, wl.d, wl.E, wl.k, 128, 128, wl.act_dtype, wl.act_dtype)
     ws = torch.empty(B.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
-    call = lambda: B.moe_route_limited(inp["x"], inp["Wg"], inp.get("bias"), a_dev, wl.k, workspace=ws)  # noqa
+    if grouped:
+        call = lambda: B.moe_route_grouped(inp["x"], inp["Wg"], inp.get("bias"), wl.k, n_group, workspace=ws)  # noqa
+    else:
+        call = lambda: B.moe_route_limited(inp["x"], inp["Wg"], inp.get("bias"), a_dev, wl.k, workspace=ws)  # noqa
     ms_per_step = wall_ms(call, args.steps, args.warmup)
     dev_ms = event_ms(call, args.steps)
     ab = 4 if wl.act_dtype == W.F32 else 2
     bytes_ = wl.T * wl.d * ab + wl.d * wl.E * 4 + wl.E + wl.T * wl.k * (4 + 4 + 4 + 4) + (2 * wl.E + 1) * 4
     flops = 2.0 * wl.T * wl.d * wl.E
-    # the router's fp32 FMA chains run on the vector ALUs (bit-exact logits), not on MFMA
-    if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (FP32_VALU_PEAK_TFLOPS * 1e12):
+    # the logits' fp32 FMA chains (bit-exact): vector ALU for few tokens, fp32 MFMA (K = 1 steps) above
+    on_mfma = wl.T > ROUTER_FEW_MAX_T
+    peak = MFMA_PEAK_TFLOPS[W.F32] if on_mfma else FP32_VALU_PEAK_TFLOPS
+    if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (peak * 1e12):
         roof = {"bound": "hbm", "achieved": bytes_ / (dev_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "alu", "achieved": flops / (dev_ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+        roof = {"bound": "mfma" if on_mfma else "alu", "achieved": flops / (dev_ms * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "whole moe_route_limited call (router logits + masked top-k + permutation)"
+    name = "moe_route_grouped" if grouped else "moe_route_limited"
+    roof["kernel"] = f"whole {name} call (router logits + {'grouped' if grouped else 'masked'} top-k + permutation)"
     roof["kernel_ms"] = dev_ms
-    out = base_record(wl, args, f"device-limited routing tokens/s ({int(allowed.sum())} of {wl.E} experts allowed)",
-                      wl.T / (ms_per_step * 1e-3), "tokens/s", ms_per_step)
+    metric = (f"group-limited routing tokens/s ({n_group} groups, {wl.k // 2} kept)" if grouped else
+              f"device-limited routing tokens/s ({int(allowed.sum())} of {wl.E} experts allowed)")
+    out = base_record(wl, args, metric, wl.T / (ms_per_step * 1e-3), "tokens/s", ms_per_step)
     out["roofline"] = roof
     out["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         from oracle import oracle as O
         h = {n: W.to_numpy(inp[n]) for n in ("x", "Wg")}
+        b = W.to_numpy(inp.get("bias"))
         t0 = time.perf_counter()
-        O.route_limited(h["x"], h["Wg"], W.to_numpy(inp.get("bias")), allowed.numpy(), wl.k, wl.act_dtype)
+        if grouped:
+            O.route_grouped(h["x"], h["Wg"], b, wl.k, n_group, wl.act_dtype)
+        else:
+            O.route_limited(h["x"], h["Wg"], b, allowed.numpy(), wl.k, wl.act_dtype)
         dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": wl.T / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
                                "omp_threads": O.num_threads(), "kind": "oracle",
-                               "sample": f"route_limited of all {wl.T} tokens ({dt:.2f} s)"}
+                               "sample": f"{'route_grouped' if grouped else 'route_limited'} of all {wl.T} tokens "
+                                         f"({dt:.2f} s)"}
     return out
 
 
@@ -417,7 +434,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=W.DECODE_BF16.name, choices=[w.name for w in W.CONFIGS])
-    ap.add_argument("--variant", default="layer", choices=["layer", "shard-ep8", "route-limited", "utilization"])
+    ap.add_argument("--variant", default="layer",
+                    choices=["layer", "shard-ep8", "route-limited", "route-grouped", "utilization"])
     ap.add_argument("--rank", type=int, default=0, choices=range(8), help="expert-parallel rank / device (of 8)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -442,8 +460,8 @@ def main():
     inp = W.generate(wl, seed=args.seed, device=dev, weights=args.variant in ("layer", "shard-ep8"))
     if args.variant in ("layer", "shard-ep8"):
         out = run_layer(wl, inp, args, dev)
-    elif args.variant == "route-limited":
-        out = run_route_limited(wl, inp, args, dev)
+    elif args.variant in ("route-limited", "route-grouped"):
+        out = run_route(wl, inp, args, dev, grouped=args.variant == "route-grouped")
     else:
         out = run_utilization(wl, inp, args, dev)
     print(json.dumps(out), flush=True)

@@ -173,6 +173,24 @@ moe_status_t moe_route_limited(const moe_shape_t* shape, const void* x, const fl
                                hipStream_t stream);
 
 /*
+ * Group-limited routing ("Technical Architecture and Core Innovations", "Architectural Breakthroughs",
+ * item 1, "Hierarchical Dynamic Routing": a two-layer gate first distributes tokens over expert groups by
+ * a softmax, then selects two experts per group).  Taken as: the E experts form n_group groups of
+ * E / n_group consecutive experts (expert e in group e / (E / n_group)); a group's candidates are its two
+ * largest logits (equal logits -> lower index) and its score is the fp32 sum of those two logits; the
+ * k / 2 groups with the largest scores are kept (equal scores -> lower group index), and the token's k
+ * experts are their candidates, in descending-logit order as moe_route's slots.  w is the softmax over
+ * those k logits, as in moe_route.  With 8 groups and k = 8 this is two experts from each of four groups.
+ *   n_group  groups: divides E, E / n_group >= 2, k even, k / 2 <= n_group, and n_group <= 16 for
+ *            E <= 256 (<= 64 above); otherwise MOE_ERR_UNSUPPORTED (n_group < 1: MOE_ERR_INVALID_ARG).
+ * All other arguments, outputs and guarantees as moe_route (the bias is added before selection).
+ */
+moe_status_t moe_route_grouped(const moe_shape_t* shape, int64_t n_group, const void* x, const float* Wg,
+                               const float* bias, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * One expert-parallel rank's share of the layer ("DeepSeek-V3.2-Exp / Mixture of experts", MoE
  * __init__ and forward excerpts: a rank owns the routed experts [experts_start_idx, experts_end_idx)
  * and a slice of the shared expert, adds their outputs into an fp32 y, and dist.all_reduce(y) sums the

@@ -15,7 +15,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP",
           5: "MOE_ERR_SCRATCH"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_staged", "moe_route_limited",
-           "moe_forward_shard", "moe_expert_utilization", "moe_forward_noalloc", "moe_status_string")
+           "moe_route_grouped", "moe_forward_shard", "moe_expert_utilization", "moe_forward_noalloc",
+           "moe_status_string")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 NUM_STAGES = 7
 STAGE_NAMES = ("router_logits", "topk_softmax", "permute", "x_quant", "up_gemm", "down_gemm", "combine")
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_limited.restype = ctypes.c_int
         L.moe_route_limited.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp]
         i64 = ctypes.c_int64
+        L.moe_route_grouped.restype = ctypes.c_int
+        L.moe_route_grouped.argtypes = [sp, i64] + [vp] * 10 + [ctypes.c_size_t, vp]
         L.moe_forward_shard.restype = ctypes.c_int
         L.moe_forward_shard.argtypes = [sp] + [vp] * 4 + [i64] * 3 + [vp] * 17 + [ctypes.c_size_t, vp, vp]
         L.moe_expert_utilization.restype = ctypes.c_int
@@ -105,10 +108,11 @@ def _workspace(shape, dev, workspace):
     return workspace, need
 
 
-def moe_route(x, Wg, bias, k, workspace=None, allowed=None):
+def moe_route(x, Wg, bias, k, workspace=None, allowed=None, n_group=None):
     """Routing of x [T, d]: returns dict(idx, w, counts, offsets, sorted_slots, pos) as device tensors.
 
-    With `allowed` (uint8 [E] device tensor) calls moe_route_limited (device-limited routing)."""
+    With `allowed` (uint8 [E] device tensor) calls moe_route_limited (device-limited routing); with
+    `n_group` moe_route_grouped (group-limited routing)."""
     T, d = x.shape
     E = Wg.shape[0]
     shape = make_shape(T, d, E, k, 128, 128, _act_code(x), _act_code(x))
@@ -120,19 +124,30 @@ def moe_route(x, Wg, bias, k, workspace=None, allowed=None):
                sorted_slots=torch.empty(T * k, **i32), pos=torch.empty(T * k, **i32))
     tail = [_ptr(out["idx"]), _ptr(out["w"]), _ptr(out["counts"]), _ptr(out["offsets"]),
             _ptr(out["sorted_slots"]), _ptr(out["pos"]), _ptr(workspace), workspace.numel(), _stream(dev)]
+    if allowed is not None and n_group is not None:
+        raise ValueError("a routing mask and group-limited routing do not combine")
     if allowed is not None:
         _check_allowed(allowed, E)
-        st = lib().moe_route_limited(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(allowed), *tail)
+        st, name = lib().moe_route_limited(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(allowed),
+                                           *tail), "moe_route_limited"
+    elif n_group is not None:
+        st, name = lib().moe_route_grouped(ctypes.byref(shape), int(n_group), _ptr(x), _ptr(Wg), _ptr(bias),
+                                           *tail), "moe_route_grouped"
     else:
-        st = lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), *tail)
+        st, name = lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), *tail), "moe_route"
     if st:
-        raise MoeError(st, "moe_route_limited" if allowed is not None else "moe_route")
+        raise MoeError(st, name)
     return out
 
 
 def moe_route_limited(x, Wg, bias, allowed, k, workspace=None):
     """Device-limited routing: moe_route with the per-expert mask `allowed` (uint8 [E] device tensor)."""
     return moe_route(x, Wg, bias, k, workspace=workspace, allowed=allowed)
+
+
+def moe_route_grouped(x, Wg, bias, k, n_group, workspace=None):
+    """Group-limited routing: two experts from each of the k / 2 best of n_group expert groups."""
+    return moe_route(x, Wg, bias, k, workspace=workspace, n_group=n_group)
 
 
 def _check_allowed(allowed, E):

@@ -125,15 +125,19 @@ extern "C" const char* moe_status_string(moe_status_t st)
         if ((expr) != hipSuccess) return MOE_ERR_HIP;    \
     } while (0)
 
-// Routing with an optional per-expert mask (allowed == NULL: every expert).
+// Routing with an optional per-expert mask (allowed == NULL: every expert), or group-limited over
+// n_group groups (n_group > 0; no mask).
 static moe_status_t route_impl(const moe_shape_t* shape, const void* x, const float* Wg, const float* bias,
-                               const uint8_t* allowed, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
-                               int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream)
+                               const uint8_t* allowed, int n_group, int32_t* idx, float* w, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_slots, int32_t* pos, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream)
 {
     moe_status_t st = check_shape(shape);
     if (st != MOE_OK) return st;
     const moe_shape_t& s = *shape;
+    if (n_group > 0 && (s.E % n_group || s.E / n_group < 2 || s.k % 2 || s.k / 2 > n_group ||
+                        n_group > (s.E <= 256 ? 16 : 64)))
+        return MOE_ERR_UNSUPPORTED;
     if (s.T == 0) return MOE_OK;
     if (!x || !Wg || !idx || !w || !counts || !offsets || !sorted_slots || !workspace) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(Wg)) return MOE_ERR_INVALID_ARG;
@@ -141,11 +145,11 @@ static moe_status_t route_impl(const moe_shape_t* shape, const void* x, const fl
     if (workspace_bytes < ws.total || ((uintptr_t)workspace & 255)) return MOE_ERR_WORKSPACE;
     const TileRange all = {0, (int)s.E, 1};
     MOE_TRY(launch_router_logits(s, x, Wg, bias, ws.logits, stream));
-    if (routing_is_fused(s)) {
+    if (n_group == 0 && routing_is_fused(s)) {
         MOE_TRY(launch_routing_fused(s, ws.logits, allowed, idx, w, counts, offsets, sorted_slots, pos ? pos : ws.pos,
                                      ws, tile_rows(s), all, stream));
     } else {
-        MOE_TRY(launch_topk(s, ws.logits, allowed, idx, w, ws, stream));
+        MOE_TRY(launch_topk(s, ws.logits, allowed, idx, w, ws, stream, n_group));
         MOE_TRY(launch_permute(s, idx, counts, offsets, sorted_slots, pos ? pos : ws.pos, ws, tile_rows(s), all,
                                stream));
     }
@@ -157,8 +161,18 @@ extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const
                                   int32_t* sorted_slots, int32_t* pos, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream)
 {
-    return route_impl(shape, x, Wg, bias, nullptr, idx, w, counts, offsets, sorted_slots, pos, workspace,
+    return route_impl(shape, x, Wg, bias, nullptr, 0, idx, w, counts, offsets, sorted_slots, pos, workspace,
                       workspace_bytes, stream);
+}
+
+extern "C" moe_status_t moe_route_grouped(const moe_shape_t* shape, int64_t n_group, const void* x, const float* Wg,
+                                          const float* bias, int32_t* idx, float* w, int32_t* counts,
+                                          int32_t* offsets, int32_t* sorted_slots, int32_t* pos, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream)
+{
+    if (n_group < 1 || n_group > 1024) return MOE_ERR_INVALID_ARG;
+    return route_impl(shape, x, Wg, bias, nullptr, (int)n_group, idx, w, counts, offsets, sorted_slots, pos,
+                      workspace, workspace_bytes, stream);
 }
 
 extern "C" moe_status_t moe_route_limited(const moe_shape_t* shape, const void* x, const float* Wg,
@@ -167,7 +181,7 @@ extern "C" moe_status_t moe_route_limited(const moe_shape_t* shape, const void* 
                                           void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!allowed) return MOE_ERR_INVALID_ARG;
-    return route_impl(shape, x, Wg, bias, allowed, idx, w, counts, offsets, sorted_slots, pos, workspace,
+    return route_impl(shape, x, Wg, bias, allowed, 0, idx, w, counts, offsets, sorted_slots, pos, workspace,
                       workspace_bytes, stream);
 }
 

@@ -117,7 +117,7 @@ Workspace carve_workspace(const moe_shape_t& s, void* base);
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
                                 float* logits, hipStream_t stream);
 hipError_t launch_topk(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
-                       const Workspace& ws, hipStream_t stream);
+                       const Workspace& ws, hipStream_t stream, int n_group = 0);
 bool routing_is_fused(const moe_shape_t& s);
 hipError_t launch_routing_fused(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
                                 int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* pos,

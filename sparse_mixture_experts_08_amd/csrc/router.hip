@@ -327,10 +327,11 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
 // once; a wavefront when E <= 1024), 64 tokens (one chunk) per block of 16 wavefronts.  Also records,
 // per chunk, which tokens chose each expert (a 64-bit mask) and how many.
 // ------------------------------------------------------------------------------------------------
-// NQ: logits per lane (E <= W * NQ).
-template <int W, int NQ>
+// NQ: logits per lane (E <= W * NQ).  GROUPED: group-limited selection over n_group groups (topk_grouped)
+// instead of the plain (optionally masked) top-k.
+template <int W, int NQ, bool GROUPED>
 __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restrict__ L, const uint8_t* __restrict__ allowed,
-                                                            int T, int E, int k,
+                                                            int T, int E, int k, int n_group,
                                                             int32_t* __restrict__ idx, float* __restrict__ w,
                                                             uint64_t* __restrict__ chunk_bits,
                                                             int32_t* __restrict__ chunk_counts)
@@ -347,7 +348,8 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
         const bool valid = t < T;                      // the W-lane group of a token past T reads token 0
         int my_e;
         float my_w;
-        topk_group<W, NQ>(L + (size_t)(valid ? t : 0) * E, allowed, E, k, sub, my_e, my_w);
+        if constexpr (GROUPED) topk_grouped<W, NQ>(L + (size_t)(valid ? t : 0) * E, E, k, n_group, sub, my_e, my_w);
+        else topk_group<W, NQ>(L + (size_t)(valid ? t : 0) * E, allowed, E, k, sub, my_e, my_w);
         if (valid && sub < k) {
             idx[(size_t)t * k + sub] = my_e;
             w[(size_t)t * k + sub] = my_w;
@@ -364,14 +366,24 @@ __global__ __launch_bounds__(1024) void topk_softmax_kernel(const float* __restr
 }
 
 hipError_t launch_topk(const moe_shape_t& s, const float* logits, const uint8_t* allowed, int32_t* idx, float* w,
-                       const Workspace& ws, hipStream_t stream)
+                       const Workspace& ws, hipStream_t stream, int n_group)
 {
-    if (s.E <= 256)
-        topk_softmax_kernel<16, 16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
-                                                                                idx, w, ws.chunk_bits, ws.chunk_counts);
-    else
-        topk_softmax_kernel<64, 16><<<(unsigned)ws.nchunks, 1024, 0, stream>>>(logits, allowed, (int)s.T, (int)s.E, (int)s.k,
-                                                                                idx, w, ws.chunk_bits, ws.chunk_counts);
+    const unsigned grid = (unsigned)ws.nchunks;
+    const int T = (int)s.T, E = (int)s.E, k = (int)s.k;
+    if (n_group > 0) {
+        if (E <= 256)
+            topk_softmax_kernel<16, 16, true><<<grid, 1024, 0, stream>>>(logits, nullptr, T, E, k, n_group, idx, w,
+                                                                          ws.chunk_bits, ws.chunk_counts);
+        else
+            topk_softmax_kernel<64, 16, true><<<grid, 1024, 0, stream>>>(logits, nullptr, T, E, k, n_group, idx, w,
+                                                                          ws.chunk_bits, ws.chunk_counts);
+    } else if (E <= 256) {
+        topk_softmax_kernel<16, 16, false><<<grid, 1024, 0, stream>>>(logits, allowed, T, E, k, 0, idx, w, ws.chunk_bits,
+                                                                       ws.chunk_counts);
+    } else {
+        topk_softmax_kernel<64, 16, false><<<grid, 1024, 0, stream>>>(logits, allowed, T, E, k, 0, idx, w, ws.chunk_bits,
+                                                                       ws.chunk_counts);
+    }
     return hipGetLastError();
 }
 

@@ -189,3 +189,23 @@ def test_route_limited_and_utilization_argument_errors():
     assert L.moe_expert_utilization(-3, *q, None) == 1
     q[2] = None
     assert L.moe_expert_utilization(8, *q, None) == 1
+
+
+def test_route_grouped_argument_errors():
+    # Every case fails on the host, before any launch (the pointers are never dereferenced).
+    L = B.lib()
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(10)]
+
+    def call(shape, n_group, ws_bytes=1 << 30):
+        return L.moe_route_grouped(ctypes.byref(shape), n_group, *p, ctypes.c_size_t(ws_bytes), None)
+
+    assert call(_shape(), 0) == 1                        # n_group < 1
+    assert call(_shape(), -8) == 1
+    assert call(_shape(k=9, E=8), 4) == 1                # the shape itself is invalid (k > E)
+    assert call(_shape(E=256, k=8), 3) == 2              # n_group does not divide E
+    assert call(_shape(E=256, k=7), 8) == 2              # odd k
+    assert call(_shape(E=256, k=8), 2) == 2              # k / 2 groups more than there are
+    assert call(_shape(E=16, k=4), 16) == 2              # one expert per group
+    assert call(_shape(E=256, k=8), 32) == 2             # more groups than lanes per token (E <= 256: 16)
+    assert call(_shape(E=512, k=8), 128) == 2            # ... (E > 256: 64)
+    assert call(_shape(), 8, ws_bytes=16) == 3           # a valid grouping with too small a workspace

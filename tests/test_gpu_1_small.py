@@ -54,15 +54,16 @@ def test_edge_shapes(wl):
 
 @pytest.mark.parametrize("T,E,act", [
     (256, 64, BF16), (257, 64, BF16),      # few-token router: 8- then 16-token blocks
-    (512, 40, F32), (513, 40, F32),        # ... then the DPP row-rotation kernel (E not a multiple of 32)
-    (513, 64, BF16), (2500, 257, BF16),    # ragged 64-token and 32-expert tails
-    (8192, 64, BF16), (8193, 72, BF16),    # DPP kernel's last size, then the 64 x 64 register tiles
+    (512, 40, F32), (513, 40, F32),        # ... then the MFMA kernel (E not a multiple of 64)
+    (513, 64, BF16), (2500, 257, BF16),    # ragged 64-token and 64-expert tails
+    (8192, 64, BF16), (8193, 72, BF16),    # many tokens, one token past a block
+    (600, 1024, BF16), (700, 1, F32),      # the largest E, and a single expert, on the matrix cores
 ], ids=lambda v: str(v))
 def test_router_kernel_boundaries(T, E, act):
-    # Routing of every token, bit for bit against the oracle, on both sides of each router kernel switch,
+    # Routing of every token, bit for bit against the oracle, on both sides of the router kernel switch,
     # with a bias (one fp32 add after the chain).
     from gpu_util import check_routing
-    wl = W.Workload("router-edge", T, 512, E, 4, 128, 128, act, act)
+    wl = W.Workload("router-edge", T, 512, E, min(4, E), 128, 128, act, act)
     inp = W.generate(wl, seed=11, device=DEV, weights=False)
     g = torch.Generator().manual_seed(T)
     inp["bias"] = (torch.randn(E, generator=g) * 0.01).to(DEV)

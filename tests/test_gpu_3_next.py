@@ -239,3 +239,57 @@ def test_utilization_of_layer_counts_and_zero_total():
     assert np.array_equal(util.cpu().numpy(), u) and np.array_equal(flags.cpu().numpy(), f)
     assert tuple(summ.cpu().tolist()) == tuple(s) and s[0] + s[1] > 0      # the skewed mix trips alerts
     assert (zu.cpu() == 0).all() and (zf.cpu() == 0).all() and zs.cpu().tolist() == [0, 0]
+
+
+# ---------------------------------------------------------------------------------------------------
+# group-limited routing
+# ---------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k,G,bias", [
+    (64, 256, 8, 8, False),     # decode size: 4 of 8 groups of 32, two experts each
+    (700, 256, 8, 8, True),     # many blocks, ragged last chunk, with a bias
+    (300, 64, 6, 4, False),     # 3 of 4 groups of 16
+    (200, 32, 4, 16, True),     # groups of two experts, the most groups 16 lanes per token hold
+    (500, 1024, 16, 64, False), # the largest E and k: 8 of 64 groups (a wavefront per token)
+    (130, 258, 6, 6, True),     # E not a power of two (43 per group), a wavefront per token
+], ids=lambda v: str(v))
+def test_grouped_routing_bit_exact(T, E, k, G, bias):
+    wl = W.Workload("grouped", T, 512, E, k, 128, 128, BF16, BF16)
+    inp = W.generate(wl, seed=41, device=DEV, weights=False)
+    if bias:
+        g = torch.Generator().manual_seed(T + E)
+        inp["bias"] = (torch.randn(E, generator=g) * 0.5).to(DEV)
+    say(f"[grouped] T={T} E={E} k={k} G={G} bias={bias}")
+    r = B.moe_route_grouped(inp["x"], inp["Wg"], inp.get("bias"), k, G)
+    torch.cuda.synchronize()
+    h = host(inp)
+    orc = O.route_grouped(h["x"], h["Wg"], h.get("bias"), k, G, BF16)
+    check_routing(wl, r, orc)
+    grp = r["idx"].cpu().numpy() // (E // G)
+    for t in range(0, T, max(1, T // 50)):
+        vals, cnt = np.unique(grp[t], return_counts=True)
+        assert len(vals) == k // 2 and (cnt == 2).all()
+
+
+def test_grouped_routing_ties_and_full_size():
+    # zero input: every logit 0 -> groups 0 .. k/2-1 and the two lowest experts of each; then the
+    # prefill configuration's full size (4096 tokens, d = 7168, 8 groups of 32) with the skewed bias
+    wl = W.Workload("grouped-zero", 100, 256, 256, 8, 128, 128, BF16, BF16)
+    inp = W.generate(wl, seed=42, device=DEV, weights=False)
+    inp["x"].zero_()
+    r = B.moe_route_grouped(inp["x"], inp["Wg"], None, 8, 8)
+    torch.cuda.synchronize()
+    assert (r["idx"].cpu() == torch.tensor([0, 1, 32, 33, 64, 65, 96, 97], dtype=torch.int32)).all()
+    assert torch.allclose(r["w"].cpu(), torch.full((100, 8), 0.125))
+    h = host(inp)
+    check_routing(wl, r, O.route_grouped(h["x"], h["Wg"], None, 8, 8, BF16))
+    wl = W.BY_NAME["prefill-bf16-T4096-d7168-E256-k8"]
+    skew = W.BY_NAME["skewed-bf16-T16384-d7168-E256-k8"]
+    inp = W.generate(wl, seed=0, device=DEV, weights=False)
+    inp["bias"] = W.generate(W.Workload("b", 1, 128, 256, 8, 128, 128, BF16, BF16, skew=True), seed=0, device=DEV,
+                             weights=False)["bias"]
+    assert skew.skew
+    say("[grouped] full size T=4096 d=7168 E=256 k=8 G=8, skewed bias")
+    r = B.moe_route_grouped(inp["x"], inp["Wg"], inp["bias"], 8, 8)
+    torch.cuda.synchronize()
+    h = host(inp)
+    check_routing(wl, r, O.route_grouped(h["x"], h["Wg"], h["bias"], 8, 8, BF16))
