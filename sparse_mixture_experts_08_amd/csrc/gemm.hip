@@ -1206,8 +1206,12 @@ static constexpr int KROT_UP16 = 0;
 static constexpr int KROT_UP = 3;
 static constexpr int KROT_WDN = 3;   // wide-kernel down GEMM (rotations 0 / 1 / 5 / 7 / 13 measured slower)
 static constexpr int KROT_DN = 1;
-// Tiles per XCD group of the large-tile block order (see grouped_gemm_kernel).
+// Tiles per XCD group of the large-tile block order (see grouped_gemm_kernel).  The fp8 down GEMM, whose
+// h rows are short (inter bytes) and whose 256-wide n-blocks are many (d / 256), does best with groups of
+// two tiles (32768-token fp8 layer: 1 / 2 / 3 / 8 tiles 5.11 / 5.08 / 5.11 / 5.31 ms, bitwise equal); the
+// bf16 down GEMM does not (skewed 4.50 -> 4.66 ms with two).
 static constexpr int GROUP_M = 8;
+static constexpr int GROUP_M_F8_DN = 2;
 
 // bf16 256-row tiles: 128-byte K stages in a ring of two (64-byte stages in deeper rings request twice
 // the lines and measured slower), eight wavefronts (four, one per SIMD with 128 x 128 each, measured
@@ -1330,6 +1334,7 @@ hipError_t launch_down_gemm(const moe_shape_t& s, const void* W2, const float* W
     // With at most one tile per expert on average no weight panel is shared between tiles: walk each
     // tile's n-blocks together instead, so its h rows are fetched once into L2.
     if (bm > 16 && s.T * s.k <= (int64_t)s.E * bm) dn.group_m = 1;
+    else if (fp8 && bm > 16) dn.group_m = GROUP_M_F8_DN;
     // 256-wide n-blocks where d allows (d is a multiple of 128; an odd multiple takes 128-wide ones)
     const bool wide = s.d % 256 == 0;
     if (bm == 16) {
