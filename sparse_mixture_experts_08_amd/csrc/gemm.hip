@@ -829,16 +829,42 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 // MID_AT's MFMAs are issued (at the end when the wavefront computes fewer row blocks): the kernel issues
 // the second half of a ring refill there.  Only the first NB of the WM row blocks hold tile rows; the
 // others get no MFMAs, no rescale and no fragment reads (their accumulators stay zero, never stored).
+// In the pipelined form (TIGHT below) a stage's last row block is not rescaled before the stage barrier:
+// its MFMA results and scale products are carried into the next stage and rescaled after that stage's
+// first row block's MFMAs, like any other block's one block later.  Each accumulator still receives its K
+// blocks' terms in K order.  The carry starts as zeros (adding 0 * 0 leaves +0 accumulators as they are)
+// and f8_flush applies the last stage's after the walk.
+template <int NP> struct F8Carry {
+    f32x4 p[NP];
+    float s1, s3;
+};
+
+template <bool UP, int WM, int WN> constexpr bool f8_tight() { return WM * WN * (UP ? 2 : 1) > 16; }
+
+template <bool UP, int WM, int WN, int NB, int NP>
+__device__ __forceinline__ void f8_flush(const F8Carry<NP>& car, f32x4 (&acc1)[WM][WN], f32x4 (&acc3)[WM][WN])
+{
+    if constexpr (f8_tight<UP, WM, WN>() && NB > 0) {
+#pragma unroll
+        for (int j = 0; j < WN; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                acc1[NB - 1][j][r] += car.p[j][r] * car.s1;
+                if constexpr (UP) acc3[NB - 1][j][r] += car.p[WN + j][r] * car.s3;
+            }
+    }
+}
+
 template <bool UP, int WM, int WN, int BN, int NB, typename MID>
 __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_lds, const float* sA_lds, float sb1,
                                        float sb3, int wm0, int wn0, int lane, f32x4 (&acc1)[WM][WN],
-                                       f32x4 (&acc3)[WM][WN], MID&& mid)
+                                       f32x4 (&acc3)[WM][WN], F8Carry<UP ? 2 * WN : WN>& car, MID&& mid)
 {
     static_assert(NB >= 0 && NB <= WM, "row blocks");
     constexpr int MID_AT = UP ? 3 : 0;
     static_assert(WM > MID_AT, "mid() runs inside the row-block loop");
     const int r16 = lane & 15, q = lane >> 4;
-    constexpr bool TIGHT = WM * WN * (UP ? 2 : 1) > 16;  // more than 64 accumulator VGPRs
+    constexpr bool TIGHT = f8_tight<UP, WM, WN>();     // more than 64 accumulator VGPRs
     auto frag = [&](const uint8_t* base, int row) {
         const i32x4 lo = *(const i32x4*)(base + swzr<128>(row, 2 * q));
         const i32x4 hi = *(const i32x4*)(base + swzr<128>(row, 2 * q + 1));
@@ -859,69 +885,70 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
     i32x8 a = frag(As_lds, wm0 + r16);
     float sa = scale(0);
     if constexpr (TIGHT) {
-        // Software pipeline over row blocks: block i's MFMAs are issued before block i - 1's results are
-        // rescaled, so the matrix pipe runs while the vector ALU rescales.  Block i + 1's A operand
-        // passes through an empty asm that also takes block i - 1's rescaled accumulators, so at most
-        // two blocks' MFMA results are live.
+        // Software pipeline over row blocks: block i's MFMAs are issued before the previous block's results
+        // are rescaled (block i - 1, or for i = 0 the previous stage's last block, from the carry), so the
+        // matrix pipe runs while the vector ALU rescales.  Block i + 1's A operand passes through an empty
+        // asm that also takes the rescaled accumulators, so at most two blocks' MFMA results are live.
         constexpr int NP = UP ? 2 * WN : WN;          // MFMA results per row block
         f32x4 pc[NP], pp[NP];
-        float s1 = 0.f, s3 = 0.f;                      // scale products of the previous block
+        float s1 = car.s1, s3 = car.s3;                // scale products of the previous block
 #pragma unroll
-        for (int i = 0; i <= NB; i++) {
+        for (int n = 0; n < NP; n++) pp[n] = car.p[n];
+#pragma unroll
+        for (int i = 0; i < NB; i++) {
+            const int ip = i > 0 ? i - 1 : NB - 1;     // the block rescaled here
             i32x8 a_next = a;
             float sa_next = sa;
-            if (i < NB) {
 #pragma unroll
-                for (int j = 0; j < WN; j++) {
-                    pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1[j], a, zero, 0, 0, 0, 127, 0, 127);
-                    if constexpr (UP)
-                        pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b3[j], a, zero, 0, 0, 0, 127, 0, 127);
-                }
-                if (UP && i == MID_AT) mid();
-                if (i + 1 < NB) {
-                    a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
-                    sa_next = scale(i + 1);
+            for (int j = 0; j < WN; j++) {
+                pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1[j], a, zero, 0, 0, 0, 127, 0, 127);
+                if constexpr (UP)
+                    pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b3[j], a, zero, 0, 0, 0, 127, 0, 127);
+            }
+            if (UP && i == MID_AT) mid();
+            if (i + 1 < NB) {
+                a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
+                sa_next = scale(i + 1);
+            }
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc1[ip][j][r] += pp[j][r] * s1;
+                if constexpr (UP) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc3[ip][j][r] += pp[WN + j][r] * s3;
                 }
             }
-            if (i > 0) {
+            if (!UP) {
+                // Down GEMM: after each MFMA of block i, four of the previous block's rescale FMAs (and block
+                // i + 1's fragment reads after the first), so the vector ALU works while the matrix
+                // pipe runs instead of both wavefronts of a SIMD rescaling at once with the pipe idle.
+                // The up GEMM, with twice the MFMAs per block, ran slower under the same grouping and
+                // keeps the compiler's order.
 #pragma unroll
-                for (int j = 0; j < WN; j++) {
-#pragma unroll
-                    for (int r = 0; r < 4; r++) acc1[i - 1][j][r] += pp[j][r] * s1;
-                    if constexpr (UP) {
-#pragma unroll
-                        for (int r = 0; r < 4; r++) acc3[i - 1][j][r] += pp[WN + j][r] * s3;
-                    }
-                }
-                if (!UP && i < NB) {
-                    // Down GEMM: after each MFMA of block i, four of block i - 1's rescale FMAs (and block
-                    // i + 1's fragment reads after the first), so the vector ALU works while the matrix
-                    // pipe runs instead of both wavefronts of a SIMD rescaling at once with the pipe idle.
-                    // The up GEMM, with twice the MFMAs per block, ran slower under the same grouping and
-                    // keeps the compiler's order.
-#pragma unroll
-                    for (int m = 0; m < NP; m++) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        if (m == 0) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < WN; j++) {
-                    if constexpr (UP) asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i - 1][j]), "v"(acc3[i - 1][j]));
-                    else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[i - 1][j]));
+                for (int m = 0; m < NP; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (m == 0) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 }
             }
-            if (!UP && i < NB && i == MID_AT) mid();
-            if (i < NB) {
-                s1 = sa * sb1;
-                s3 = sa * sb3;
 #pragma unroll
-                for (int n = 0; n < NP; n++) pp[n] = pc[n];
-                a = a_next;
-                sa = sa_next;
+            for (int j = 0; j < WN; j++) {
+                if constexpr (UP) asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[ip][j]), "v"(acc3[ip][j]));
+                else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[ip][j]));
             }
+            if (!UP && i == MID_AT) mid();
+            s1 = sa * sb1;
+            s3 = sa * sb3;
+#pragma unroll
+            for (int n = 0; n < NP; n++) pp[n] = pc[n];
+            a = a_next;
+            sa = sa_next;
         }
+#pragma unroll
+        for (int n = 0; n < NP; n++) car.p[n] = pp[n];
+        car.s1 = s1;
+        car.s3 = s3;
         if constexpr (NB <= MID_AT) mid();
         return;
     }
@@ -1133,12 +1160,16 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     // stays one straight-line schedule; the walk is instantiated per count, like the bf16 kernel's).
     auto k_walk = [&](auto nb_tag) {
         constexpr int NB = decltype(nb_tag)::value;
+        F8Carry<UP ? 2 * WN : WN> car;
+#pragma unroll
+        for (int n = 0; n < (UP ? 2 * WN : WN); n++) car.p[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        car.s1 = car.s3 = 0.f;
         int buf = 0, pbuf = -1, pst = 0;
         for (int s = 0; s < nstages; s++) {
             const float* sc = scl[buf];
             const uint8_t* st = ring + buf * STAGE;
             mma_f8<UP, WM, WN, BN, NB>(st, st + BM * 128, sc, sc[BM + cb], UP ? sc[BM + 64 + cb] : 0.f, wm0, wn0, lane,
-                                       acc1, acc3, [&] { if (pbuf >= 0) issue(pbuf, pst, PERW / 2, PERW, true); });
+                                       acc1, acc3, car, [&] { if (pbuf >= 0) issue(pbuf, pst, PERW / 2, PERW, true); });
             pbuf = -1;
             if (s + 1 < nstages) {
                 wait_vmcnt<(NSTG - 2) * NL>();         // stage s + 1 has landed
@@ -1149,6 +1180,7 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
                 buf = buf + 1 == NSTG ? 0 : buf + 1;
             }
         }
+        f8_flush<UP, WM, WN, NB>(car, acc1, acc3);
     };
     with_count<WM>(nrb, k_walk);
     wait_vmcnt<0>();                                   // no load may still target this block's LDS
