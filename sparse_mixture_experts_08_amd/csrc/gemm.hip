@@ -1049,8 +1049,8 @@ __device__ __forceinline__ void f8_epilogue(const GemmArgs& g, uint8_t* smem, co
 // ---------------------------------------------------------------------------------------------------
 // fp8 form with direct-to-LDS staging (128- or 256-row tiles, eight wavefronts as 2 x 4, the 16x16x128
 // fp8 MFMA and per-K-block rescaling of mma_f8).  A K stage is 128 fp8 elements: one 128-byte line of every A
-// row, W1 row and W3 row, stored as in grouped_gemm_kernel (16-byte chunks XOR-swizzled by row), so
-// mma_stage reads it unchanged.  The stages sit in a ring of NSTG buffers filled by global_load_lds (no
+// row, W1 row and W3 row, its 16-byte chunks XOR-swizzled over a 16-row period (swzr<128>), so the 16-row
+// fragment reads of mma_f8 hit distinct banks.  The stages sit in a ring of NSTG buffers filled by global_load_lds (no
 // staging registers, no LDS stores), NSTG - 1 of them in flight while one is computed.  The scales of a
 // stage ride in the same ring: wavefronts 0-1 copy the A row scales of the stage (one 4-byte load per
 // row), wavefront 2 the W1 block scales, wavefront 3 the W3 block scales, the others a dummy copy, so
