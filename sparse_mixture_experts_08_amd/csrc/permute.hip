@@ -13,6 +13,7 @@
 // Two paths: up to 256 tokens, one block does top-k, masks, scans, scatter and tiles in one launch;
 // beyond that, a top-k kernel per chunk (router.hip), a per-expert scan over the chunks, and a scatter
 // kernel whose every block scans the expert counts itself (block 0 also stores offsets and the tiles).
+// Group-limited routing takes the second path at every token count.
 #include "moe_common.h"
 #include "topk.h"
 
