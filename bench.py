@@ -83,7 +83,7 @@ def measured_peaks(dev, read_gib=16, reps=3):
     nbytes = read_gib << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
-    grid = 256 * 16
+    grid = 8192
 
     def read():
         if L.moe_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, grid, ctypes.c_void_p(sink.data_ptr()),
@@ -108,7 +108,8 @@ def measured_peaks(dev, read_gib=16, reps=3):
                                   for _ in range(reps))
     del a, b, c
     torch.cuda.empty_cache()
-    out["how"] = (f"streaming read of {read_gib} GiB ({grid} blocks of 256 threads, 16-byte loads); 2048 wavefronts "
+    out["how"] = (f"streaming read of {read_gib} GiB ({grid} blocks of 256 threads, each reading 256 KB chunks with "
+                  "16-byte loads); 2048 wavefronts "
                   "x 8 chains of back-to-back v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_16x16x128_f8f6f4; "
                   "torch.matmul bf16 8192^3; best of 3")
     return out

@@ -14,21 +14,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// Every thread reads 16-byte vectors, four in flight per iteration, grid-stride over the buffer, and folds
-// them into an xor; the fold is stored only when it equals a value no finite buffer of ones produces, so
-// the loads cannot be removed and nothing is written in practice.
+// Block b reads the 256 KB chunks b, b + grid, b + 2 grid, ... of the buffer, each thread eight 16-byte
+// vectors in flight per step, and folds them into an xor; the fold is stored only when it equals a value no
+// finite buffer of ones produces, so the loads cannot be removed and nothing is written in practice.
+// Contiguous chunks per block stream faster than a grid-stride walk over the whole buffer (8192 blocks:
+// 6.36 against 5.8-6.2 TB/s for grid strides of 2048-16384 blocks on MI355X).
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, uint64_t n16, uint32_t* sink)
 {
-    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    constexpr uint64_t CH16 = (256u << 10) / 16;       // 16-byte vectors per chunk
+    constexpr int U = 8;
     uint32_t acc = 0;
-    uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 a = p[i];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    for (uint64_t c = blockIdx.x; c * CH16 < n16; c += gridDim.x) {
+        const uint64_t end = min((c + 1) * CH16, n16);
+        for (uint64_t i = c * CH16 + threadIdx.x; i < end; i += U * 256) {
+            uint4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) v[u] = i + u * 256 < end ? p[i + u * 256] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < U; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        }
     }
     if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
