@@ -209,3 +209,4 @@ def test_route_grouped_argument_errors():
     assert call(_shape(E=256, k=8), 32) == 2             # more groups than lanes per token (E <= 256: 16)
     assert call(_shape(E=512, k=8), 128) == 2            # ... (E > 256: 64)
     assert call(_shape(), 8, ws_bytes=16) == 3           # a valid grouping with too small a workspace
+    assert call(_shape(T=0), 8, ws_bytes=0) == 0         # no tokens: a no-op (nothing is read or launched)
