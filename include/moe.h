@@ -249,6 +249,8 @@ moe_status_t moe_expert_utilization(int64_t E, const int32_t* counts, float* uti
  *    before any device work.  Argument errors as moe_forward.
  *  - The call allocates and frees nothing.  Its first call on a device looks up the array's device
  *    address there (hipGetSymbolAddress); failure returns MOE_ERR_HIP.
+ *  - The array used is the current device's (hipGetDevice): `stream` must belong to that device (the
+ *    null stream does), as every pointer argument must point to its memory.
  *  - Every call on one GPU uses that GPU's one array, which keeps the last call's contents (no call reads
  *    what an earlier one left: nothing in it needs clearing).  Calls that overlap on one GPU -- on
  *    different streams, or from different host threads without ordering -- race on it: serialise them,

@@ -205,10 +205,12 @@ def moe_forward_noalloc(x, Wg, bias, W1, W3, W2, S1, S3, S2, k, scales=None, y=N
         r = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
                  w=torch.empty((T, k), dtype=torch.float32, device=dev),
                  counts=torch.empty(E, dtype=torch.int32, device=dev))
-    st = lib().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(W1), _ptr(W3), _ptr(W2),
-                                   _ptr(sc.get("W1s")), _ptr(sc.get("W3s")), _ptr(sc.get("W2s")), _ptr(S1), _ptr(S3),
-                                   _ptr(S2), _ptr(sc.get("S1s")), _ptr(sc.get("S3s")), _ptr(sc.get("S2s")), _ptr(y),
-                                   _ptr(r and r["idx"]), _ptr(r and r["w"]), _ptr(r and r["counts"]), _stream(dev))
+    with torch.cuda.device(dev):      # the library uses the current device's scratch array
+        st = lib().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(W1), _ptr(W3),
+                                       _ptr(W2), _ptr(sc.get("W1s")), _ptr(sc.get("W3s")), _ptr(sc.get("W2s")),
+                                       _ptr(S1), _ptr(S3), _ptr(S2), _ptr(sc.get("S1s")), _ptr(sc.get("S3s")),
+                                       _ptr(sc.get("S2s")), _ptr(y), _ptr(r and r["idx"]), _ptr(r and r["w"]),
+                                       _ptr(r and r["counts"]), _stream(dev))
     if st:
         raise MoeError(st, "moe_forward_noalloc")
     return (y, r) if routing else y
