@@ -50,3 +50,29 @@ def test_bench_json_line():
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cb, key
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+
+
+@pytest.mark.parametrize("variant", ["route-limited", "route-grouped", "utilization"])
+def test_bench_variant_json_line(variant):
+    # the rows beyond the core layer, each one JSON line with a roofline and the oracle timed beside it
+    sys.path.insert(0, ROOT)
+    import bench
+    argv = sys.argv
+    sys.argv = ["bench.py", "--workload", "tiny-fp32-T128-d512-E32-k4", "--variant", variant, "--steps", "3",
+                "--warmup", "1", "--no-peaks"]
+    buf = io.StringIO()
+    try:
+        with contextlib.redirect_stdout(buf):
+            bench.main()
+    finally:
+        sys.argv = argv
+    lines = [l for l in buf.getvalue().splitlines() if l.strip()]
+    assert len(lines) == 1, lines
+    r = json.loads(lines[0])
+    assert r["value"] > 0 and r["ms_per_step"] > 0 and r["n_gpus"] == 1
+    roof = r["roofline"]
+    assert roof["achieved"] > 0 and roof["peak"] > 0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) <= 1e-6 * max(1.0, roof["frac"])
+    assert r["cpu_baseline"]["kind"] == "oracle" and r["cpu_baseline"]["value"] > 0
+    if variant == "route-grouped":
+        assert "group-limited" in r["metric"]
