@@ -173,6 +173,22 @@ moe_status_t moe_route_limited(const moe_shape_t* shape, const void* x, const fl
                                hipStream_t stream);
 
 /*
+ * fp8 activation quantisation, the layer's step for activations entering an fp8 linear (the fp8
+ * configuration's 1 x 128 activation groups; "DeepSeek-V3.2-Exp / Mixture of experts / Shared expert",
+ * the FP8 block-scale note under the parameter table: the checkpoint's weights carry block scales), on its
+ * own: for every row and every group of 128 consecutive columns, s = amax / 448 in fp32 (s = 1 when the
+ * group is all zeros) and q = E4M3(v / s), v / s an IEEE fp32 division, rounded to nearest even and
+ * saturated to +-448 (OCP E4M3 "FN": no infinities).  moe_forward applies the same rule to x and to h.
+ *   x       [rows, cols] bf16 (uint16 bit patterns), 16-byte aligned
+ *   q       [rows, cols] E4M3 codes (uint8), 16-byte aligned (written)
+ *   scales  [rows, cols / 128] fp32 (written)
+ * cols a positive multiple of 128 (else MOE_ERR_UNSUPPORTED), rows >= 0 (rows = 0: a no-op).  Null or
+ * misaligned pointers return MOE_ERR_INVALID_ARG before any launch.
+ */
+moe_status_t moe_quantize_e4m3(int64_t rows, int64_t cols, const void* x, uint8_t* q, float* scales,
+                               hipStream_t stream);
+
+/*
  * Group-limited routing ("Technical Architecture and Core Innovations", "Architectural Breakthroughs",
  * item 1, "Hierarchical Dynamic Routing": a two-layer gate first distributes tokens over expert groups by
  * a softmax, then selects two experts per group).  Taken as: the E experts form n_group groups of

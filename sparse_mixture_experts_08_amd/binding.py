@@ -16,7 +16,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
           5: "MOE_ERR_SCRATCH"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_staged", "moe_route_limited",
            "moe_route_grouped", "moe_forward_shard", "moe_expert_utilization", "moe_forward_noalloc",
-           "moe_status_string")
+           "moe_quantize_e4m3", "moe_status_string")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 NUM_STAGES = 7
 STAGE_NAMES = ("router_logits", "topk_softmax", "permute", "x_quant", "up_gemm", "down_gemm", "combine")
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         i64 = ctypes.c_int64
         L.moe_route_grouped.restype = ctypes.c_int
         L.moe_route_grouped.argtypes = [sp, i64] + [vp] * 10 + [ctypes.c_size_t, vp]
+        L.moe_quantize_e4m3.restype = ctypes.c_int
+        L.moe_quantize_e4m3.argtypes = [i64, i64, vp, vp, vp, vp]
         L.moe_forward_shard.restype = ctypes.c_int
         L.moe_forward_shard.argtypes = [sp] + [vp] * 4 + [i64] * 3 + [vp] * 17 + [ctypes.c_size_t, vp, vp]
         L.moe_expert_utilization.restype = ctypes.c_int
@@ -143,6 +145,20 @@ def moe_route(x, Wg, bias, k, workspace=None, allowed=None, n_group=None):
 def moe_route_limited(x, Wg, bias, allowed, k, workspace=None):
     """Device-limited routing: moe_route with the per-expert mask `allowed` (uint8 [E] device tensor)."""
     return moe_route(x, Wg, bias, k, workspace=workspace, allowed=allowed)
+
+
+def moe_quantize_e4m3(x):
+    """fp8 activation quantisation of a bf16 [rows, cols] device tensor: (E4M3 codes uint8 [rows, cols],
+    fp32 scales [rows, cols / 128])."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bf16 tensor")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, max(cols // 128, 0)), dtype=torch.float32, device=x.device)
+    st = lib().moe_quantize_e4m3(rows, cols, _ptr(x), _ptr(q), _ptr(s), _stream(x.device))
+    if st:
+        raise MoeError(st, "moe_quantize_e4m3")
+    return q, s
 
 
 def moe_route_grouped(x, Wg, bias, k, n_group, workspace=None):

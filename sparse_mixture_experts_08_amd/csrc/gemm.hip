@@ -1217,11 +1217,16 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     if (sub == 0) xs[gi] = sc;
 }
 
+hipError_t launch_quantize_e4m3(int64_t rows, int cols, const void* x, uint8_t* q, float* scales, hipStream_t stream)
+{
+    const int64_t ngroups = rows * (cols / 128);
+    act_quant_kernel<<<(unsigned)((ngroups + 15) / 16), 256, 0, stream>>>((const uint16_t*)x, ngroups, cols, q, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace& ws, hipStream_t stream)
 {
-    const int64_t ngroups = s.T * (s.d / 128);
-    act_quant_kernel<<<(unsigned)((ngroups + 15) / 16), 256, 0, stream>>>((const uint16_t*)x, ngroups, (int)s.d, ws.xq, ws.xs);
-    return hipGetLastError();
+    return launch_quantize_e4m3(s.T, (int)s.d, x, ws.xq, ws.xs, stream);
 }
 
 template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N, int NBUF = 2, int MINW = 1>

@@ -303,6 +303,17 @@ extern "C" moe_status_t moe_forward_shard(const moe_shape_t* shape, const void* 
                       events);
 }
 
+extern "C" moe_status_t moe_quantize_e4m3(int64_t rows, int64_t cols, const void* x, uint8_t* q, float* scales,
+                                          hipStream_t stream)
+{
+    if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+    if (cols % 128 || cols > (1 << 30) || rows > ((int64_t)1 << 40) / cols) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!x || !q || !scales || !aligned16(x) || !aligned16(q) || ((uintptr_t)scales & 3)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_quantize_e4m3(rows, (int)cols, x, q, scales, stream));
+    return MOE_OK;
+}
+
 extern "C" moe_status_t moe_expert_utilization(int64_t E, const int32_t* counts, float* util, int32_t* flags,
                                                int32_t* summary, hipStream_t stream)
 {

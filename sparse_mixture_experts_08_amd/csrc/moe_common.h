@@ -126,6 +126,7 @@ hipError_t launch_permute(const moe_shape_t& s, const int32_t* idx, int32_t* cou
                           int32_t* sorted_slots, int32_t* pos, const Workspace& ws, int bm, TileRange tr,
                           hipStream_t stream);
 hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace& ws, hipStream_t stream);
+hipError_t launch_quantize_e4m3(int64_t rows, int cols, const void* x, uint8_t* q, float* scales, hipStream_t stream);
 // e_base: the expert stored first in W1/W3/W2 (0 for the whole layer); n_shared: the shared hidden
 // features held in S1/S3 ([n_shared, d]) and S2 ([d, n_shared]).
 hipError_t launch_up_gemm(const moe_shape_t& s, const void* x, const void* W1, const void* W3, const float* W1s,

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libmoe.s
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -210,3 +210,15 @@ def test_route_grouped_argument_errors():
     assert call(_shape(E=512, k=8), 128) == 2            # ... (E > 256: 64)
     assert call(_shape(), 8, ws_bytes=16) == 3           # a valid grouping with too small a workspace
     assert call(_shape(T=0), 8, ws_bytes=0) == 0         # no tokens: a no-op (nothing is read or launched)
+
+
+def test_quantize_e4m3_argument_errors():
+    L = B.lib()
+    x, q, s = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    assert L.moe_quantize_e4m3(-1, 128, x, q, s, None) == 1
+    assert L.moe_quantize_e4m3(4, 0, x, q, s, None) == 1
+    assert L.moe_quantize_e4m3(4, 100, x, q, s, None) == 2         # cols not a multiple of 128
+    assert L.moe_quantize_e4m3(4, 256, None, q, s, None) == 1
+    assert L.moe_quantize_e4m3(4, 256, ctypes.c_void_p(0x1008), q, s, None) == 1   # x not 16-byte aligned
+    assert L.moe_quantize_e4m3(4, 256, x, q, ctypes.c_void_p(0x3002), None) == 1   # scales not 4-byte aligned
+    assert L.moe_quantize_e4m3(0, 256, None, None, None, None) == 0  # no rows: a no-op

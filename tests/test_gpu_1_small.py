@@ -211,3 +211,35 @@ def test_hip_graph_capture_and_replay(wl):
         y_eager = B.forward_inputs(inp, wl.k)
         torch.cuda.synchronize()
         assert torch.equal(y_eager.view(torch.int16), y_ref.view(torch.int16))
+
+
+def test_activation_quantisation_bit_exact():
+    # The fp8 activation rule on its own (moe_quantize_e4m3): per row and 128-column group s = amax / 448
+    # (1 for an all-zero group) and q = E4M3(v / s), IEEE division, nearest even, saturating.  Codes and
+    # scales bit for bit against the oracle: seeded rows over many decades of magnitude, and groups built
+    # so that s is a power of two (amax = 448 * 2^j) and v / s is exact, with v / s on E4M3 midpoints (ties
+    # to even), in the subnormal range, at the top of the range and just below it.
+    from oracle import oracle as O
+    g = torch.Generator().manual_seed(7)
+    rows, cols = 300, 1024
+    x = (torch.randn(rows, cols, generator=g) * torch.exp(torch.randn(rows, 1, generator=g) * 4)).to(torch.bfloat16)
+    x[0] = 0                                          # all-zero groups: s = 1, codes 0
+    x[1, :128] = -0.0
+    mids = [1.0625, 1.1875, 1.3125, 1.4375, 1.5625, 1.6875, 1.8125, 1.9375, 3.0625, 9.5, 104.0, 432.0, 440.0,
+            446.0, 447.0, 448.0]                      # midpoints of E4M3 neighbours, and the top of the range
+    subn = [k / 1024 for k in range(1, 16)]           # multiples of 2^-10: E4M3 subnormal values and midpoints
+    for r, j in enumerate(range(-20, 20, 4)):
+        row = 2 + r
+        vals = torch.tensor(mids + subn + [-v for v in mids] + [448.0], dtype=torch.float32) * 2.0 ** j
+        x[row, :vals.numel()] = vals.to(torch.bfloat16)
+        x[row, vals.numel():128] = 0
+    xd = x.to(DEV)
+    q, s = B.moe_quantize_e4m3(xd)
+    torch.cuda.synchronize()
+    q_ref, s_ref = O.quantize_rows_e4m3(x.float().numpy())
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref), int((q.cpu().numpy() != q_ref).sum())
+    assert (s_ref[0] == 1.0).all() and (q_ref[0] == 0).all()
+    # the layer applies the same rule: zero rows still quantise, and an empty call is a no-op
+    q0, s0 = B.moe_quantize_e4m3(xd[:0])
+    assert q0.numel() == 0 and s0.numel() == 0
