@@ -335,6 +335,15 @@ def run_layer(wl, inp, args, dev):
                     "TFLOP_per_s": alg["layer_flops"] / (ms_per_step * 1e-3) / 1e12,
                     "stage_ms": {n: float(v) for n, v in zip(B.STAGE_NAMES, stage_ms)},
                     "down_gemm_GB_per_s": alg["dn_bytes"] / (dn_ms * 1e-3) / 1e9 if dn_ms > 0 else None}
+    # the gate's logits on their own roofline: fp32 FMA chains on the vector ALU up to ROUTER_FEW_MAX_T
+    # tokens, fp32 MFMA (K = 1 steps) above
+    router_ms = stage_ms[0]
+    if router_ms > 0:
+        on_mfma = wl.T > ROUTER_FEW_MAX_T
+        rpeak = MFMA_PEAK_TFLOPS[W.F32] if on_mfma else FP32_VALU_PEAK_TFLOPS
+        rt = 2.0 * wl.T * wl.d * wl.E / (router_ms * 1e-3) / 1e12
+        out["layer"]["router"] = {"unit": "mfma fp32" if on_mfma else "valu fp32", "TFLOP_per_s": rt,
+                                  "peak_TFLOPs": rpeak, "frac": rt / rpeak}
     out["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens, shard, args.cpu_seconds)

@@ -46,6 +46,8 @@ def test_bench_json_line():
     assert pk["mfma_fp8_TFLOPs"] <= 5000 * 1.02
     if "peak_measured" in roof:
         assert abs(roof["frac_measured"] - roof["achieved"] / roof["peak_measured"]) <= 1e-6 * max(1.0, roof["frac_measured"])
+    rt = r["layer"]["router"]
+    assert rt["unit"] == "valu fp32" and rt["TFLOP_per_s"] > 0 and abs(rt["frac"] - rt["TFLOP_per_s"] / rt["peak_TFLOPs"]) < 1e-9
     cb = r["cpu_baseline"]
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cb, key
