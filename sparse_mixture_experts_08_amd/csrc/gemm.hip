@@ -822,12 +822,12 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 // features 4 (l / 16) + r, r = 0..3, of token l % 16.  All four values of a lane then share one row
 // scale, and the per-K-block rescale acc += p * (row scale * weight block scale) needs one scale product
 // per lane and row block (against four rows per lane in [token][feature] order: 2 instead of 8 multiplies
-// per four MFMAs).  B fragments of the stage stay in registers; A fragments and the row scale are read
-// one row block ahead.  With more than 64 accumulator VGPRs a row block's MFMAs also wait for the
-// rescaling of the previous block's results, so only one block's MFMA results are live and a 128 x 64
-// wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.  mid() runs once row block
-// MID_AT's MFMAs are issued (at the end when the wavefront computes fewer row blocks): the kernel issues
-// the second half of a ring refill there.  Only the first NB of the WM row blocks hold tile rows; the
+// per four MFMAs).  B fragments and the lane's row scales of the stage stay in registers; A fragments are
+// read one row block ahead (two in the pipelined form).  With more than 64 accumulator VGPRs a row
+// block's MFMAs also wait for the rescaling of the previous block's results, so only one block's MFMA
+// results are live and a 128 x 64 wavefront tile (128 accumulator VGPRs) fits two wavefronts per SIMD.
+// mid() runs once in the stage, at row block MID_AT (at the end when the wavefront computes fewer row
+// blocks): the kernel issues the second half of a ring refill there.  Only the first NB of the WM row blocks hold tile rows; the
 // others get no MFMAs, no rescale and no fragment reads (their accumulators stay zero, never stored).
 // In the pipelined form (TIGHT below) a stage's last row block is not rescaled before the stage barrier:
 // its MFMA results and scale products are carried into the next stage and rescaled after that stage's
@@ -855,13 +855,12 @@ __device__ __forceinline__ void f8_flush(const F8Carry<NP>& car, f32x4 (&acc1)[W
     }
 }
 
-template <bool UP, int WM, int WN, int BN, int NB, typename MID>
+template <bool UP, int WM, int WN, int BN, int NB, int MID_AT, typename MID>
 __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_lds, const float* sA_lds, float sb1,
                                        float sb3, int wm0, int wn0, int lane, f32x4 (&acc1)[WM][WN],
                                        f32x4 (&acc3)[WM][WN], F8Carry<UP ? 2 * WN : WN>& car, MID&& mid)
 {
     static_assert(NB >= 0 && NB <= WM, "row blocks");
-    constexpr int MID_AT = UP ? 3 : 0;
     static_assert(WM > MID_AT, "mid() runs inside the row-block loop");
     const int r16 = lane & 15, q = lane >> 4;
     constexpr bool TIGHT = f8_tight<UP, WM, WN>();     // more than 64 accumulator VGPRs
@@ -876,7 +875,14 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
         b1[j] = frag(Bs_lds, wn0 + j * 16 + r16);
         if constexpr (UP) b3[j] = frag(Bs_lds, BN + wn0 + j * 16 + r16);
     }
-    auto scale = [&](int i) { return sA_lds[wm0 + i * 16 + r16]; };   // row scale of the lane's token
+    // The lane's WM row scales (rows wm0 + 16 i + r16) sit side by side in the stage's scale copy, so
+    // 16-byte reads at the start of the stage fetch them all.  A 4-byte read per row block, issued with
+    // the next A fragment, made each scale product wait for that fragment too (LDS reads complete in order).
+    static_assert(WM % 4 == 0, "row scales as 16-byte vectors");
+    f32x4 sv[WM / 4];
+#pragma unroll
+    for (int v = 0; v < WM / 4; v++) sv[v] = *(const f32x4*)(sA_lds + wm0 + r16 * WM + 4 * v);
+    auto scale = [&](int i) { return sv[i >> 2][i & 3]; };   // row scale of the lane's token in row block i
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if constexpr (NB == 0) {
         mid();
@@ -887,18 +893,20 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
     if constexpr (TIGHT) {
         // Software pipeline over row blocks: block i's MFMAs are issued before the previous block's results
         // are rescaled (block i - 1, or for i = 0 the previous stage's last block, from the carry), so the
-        // matrix pipe runs while the vector ALU rescales.  Block i + 1's A operand passes through an empty
-        // asm that also takes the rescaled accumulators, so at most two blocks' MFMA results are live.
+        // matrix pipe runs while the vector ALU rescales.  A fragments are read two blocks ahead; block
+        // i + 2's passes through an empty asm that also takes the rescaled accumulators, so its read has
+        // landed by the end of block i and at most two blocks' MFMA results are live.
         constexpr int NP = UP ? 2 * WN : WN;          // MFMA results per row block
         f32x4 pc[NP], pp[NP];
         float s1 = car.s1, s3 = car.s3;                // scale products of the previous block
 #pragma unroll
         for (int n = 0; n < NP; n++) pp[n] = car.p[n];
+        i32x8 a2 = a;                                  // block i + 1's A fragment, read one block early
+        if (NB > 1) a2 = frag(As_lds, wm0 + 16 + r16);
 #pragma unroll
         for (int i = 0; i < NB; i++) {
             const int ip = i > 0 ? i - 1 : NB - 1;     // the block rescaled here
-            i32x8 a_next = a;
-            float sa_next = sa;
+            const i32x8 a_next = a2;
 #pragma unroll
             for (int j = 0; j < WN; j++) {
                 pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1[j], a, zero, 0, 0, 0, 127, 0, 127);
@@ -906,10 +914,7 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                     pc[WN + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b3[j], a, zero, 0, 0, 0, 127, 0, 127);
             }
             if (UP && i == MID_AT) mid();
-            if (i + 1 < NB) {
-                a_next = frag(As_lds, wm0 + (i + 1) * 16 + r16);
-                sa_next = scale(i + 1);
-            }
+            if (i + 2 < NB) a2 = frag(As_lds, wm0 + (i + 2) * 16 + r16);
 #pragma unroll
             for (int j = 0; j < WN; j++) {
 #pragma unroll
@@ -919,31 +924,28 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
                     for (int r = 0; r < 4; r++) acc3[ip][j][r] += pp[WN + j][r] * s3;
                 }
             }
-            if (!UP) {
-                // Down GEMM: after each MFMA of block i, four of the previous block's rescale FMAs (and block
-                // i + 1's fragment reads after the first), so the vector ALU works while the matrix
-                // pipe runs instead of both wavefronts of a SIMD rescaling at once with the pipe idle.
-                // The up GEMM, with twice the MFMAs per block, ran slower under the same grouping and
-                // keeps the compiler's order.
+            // After each MFMA of block i, four of the previous block's rescale FMAs (and block i + 2's
+            // fragment reads after the first), so the vector ALU works while the matrix pipe runs.  The
+            // scheduling barrier at the end of the block keeps the compiler from hoisting block i's own
+            // rescale (next block's work) up to just behind its MFMAs, where it would wait for their results.
 #pragma unroll
-                for (int m = 0; m < NP; m++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (m == 0) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                }
+            for (int m = 0; m < NP; m++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (m == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
 #pragma unroll
             for (int j = 0; j < WN; j++) {
-                if constexpr (UP) asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[ip][j]), "v"(acc3[ip][j]));
-                else asm volatile("" : "+v"(a_next), "+v"(sa_next) : "v"(acc1[ip][j]));
+                if constexpr (UP) asm volatile("" : "+v"(a2) : "v"(acc1[ip][j]), "v"(acc3[ip][j]));
+                else asm volatile("" : "+v"(a2) : "v"(acc1[ip][j]));
             }
             if (!UP && i == MID_AT) mid();
-            s1 = sa * sb1;
-            s3 = sa * sb3;
+            s1 = scale(i) * sb1;
+            s3 = scale(i) * sb3;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = 0; n < NP; n++) pp[n] = pc[n];
             a = a_next;
-            sa = sa_next;
         }
 #pragma unroll
         for (int n = 0; n < NP; n++) car.p[n] = pp[n];
@@ -1120,7 +1122,11 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     }
     // scale copy of this wavefront: byte offset from its base, the base moved by the K stage below
     uint32_t soff = 0;
-    if (wave < SW) soff = (uint32_t)s_tok[wave * 64 + lane] * (uint32_t)g.ldas * 4u;
+    if (wave < SW) {
+        // A row scales in the order mma_f8 reads them: position wm0 + WM r16 + i holds row wm0 + 16 i + r16
+        const int p = wave * 64 + lane, rem = p % (WM * 16);
+        soff = (uint32_t)s_tok[p - rem + (rem % WM) * 16 + rem / WM] * (uint32_t)g.ldas * 4u;
+    }
     else if (wave == SW || (UP && wave == SW + 1)) soff = (uint32_t)(lane < BN / 128 ? lane : 0) * (uint32_t)nkb * 4u;
 
     const int nstages = K / 128;
@@ -1168,8 +1174,9 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
         for (int s = 0; s < nstages; s++) {
             const float* sc = scl[buf];
             const uint8_t* st = ring + buf * STAGE;
-            mma_f8<UP, WM, WN, BN, NB>(st, st + BM * 128, sc, sc[BM + cb], UP ? sc[BM + 64 + cb] : 0.f, wm0, wn0, lane,
-                                       acc1, acc3, car, [&] { if (pbuf >= 0) issue(pbuf, pst, PERW / 2, PERW, true); });
+            mma_f8<UP, WM, WN, BN, NB, UP ? 3 : 0>(st, st + BM * 128, sc, sc[BM + cb], UP ? sc[BM + 64 + cb] : 0.f,
+                                                   wm0, wn0, lane, acc1, acc3, car,
+                                                   [&] { if (pbuf >= 0) issue(pbuf, pst, PERW / 2, PERW, true); });
             pbuf = -1;
             if (s + 1 < nstages) {
                 wait_vmcnt<(NSTG - 2) * NL>();         // stage s + 1 has landed
