@@ -109,7 +109,7 @@ def measured_peaks(dev, read_gib=16, reps=3):
     del a, b, c
     torch.cuda.empty_cache()
     out["how"] = (f"streaming read of {read_gib} GiB ({grid} blocks of 256 threads, each reading 256 KB chunks with "
-                  "16-byte loads); 2048 wavefronts "
+                  "16-byte non-temporal loads); 2048 wavefronts "
                   "x 8 chains of back-to-back v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_16x16x128_f8f6f4; "
                   "torch.matmul bf16 8192^3; best of 3")
     return out

@@ -21,7 +21,7 @@ extern "C" {
 
 /*
  * Streaming read: `grid` blocks of 256 threads read all `bytes` of `buf` (16-byte aligned) once, block b
- * the 256 KB chunks b, b + grid, ..., with 16-byte loads, eight in flight per thread.  sink: [grid]
+ * the 256 KB chunks b, b + grid, ..., with 16-byte non-temporal loads, eight in flight per thread.  sink: [grid]
  * uint32 device array (practically never written).
  * Bytes / elapsed time is the read rate; with a buffer far beyond the 256 MB last-level cache it is the
  * HBM read ceiling.

@@ -13,13 +13,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Block b reads the 256 KB chunks b, b + grid, b + 2 grid, ... of the buffer, each thread eight 16-byte
 // vectors in flight per step, and folds them into an xor; the fold is stored only when it equals a value no
 // finite buffer of ones produces, so the loads cannot be removed and nothing is written in practice.
-// Contiguous chunks per block stream faster than a grid-stride walk over the whole buffer (8192 blocks:
-// 6.36 against 5.8-6.2 TB/s for grid strides of 2048-16384 blocks on MI355X).
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, uint64_t n16, uint32_t* sink)
+// The loads carry the non-temporal hint, which streams faster on MI355X (4 GiB, 8192 blocks: 7.1 against
+// 6.4 TB/s without it); contiguous chunks per block stream faster than a grid-stride walk over the whole
+// buffer (6.0 / 5.6-5.7 TB/s for grids of 8192 / 2048 blocks, without the hint), and 64 KB - 4 MB chunks,
+// 16 vectors in flight or 512- and 1024-thread blocks reach no more.
+__global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* __restrict__ p, uint64_t n16, uint32_t* sink)
 {
     constexpr uint64_t CH16 = (256u << 10) / 16;       // 16-byte vectors per chunk
     constexpr int U = 8;
@@ -27,9 +30,10 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
     for (uint64_t c = blockIdx.x; c * CH16 < n16; c += gridDim.x) {
         const uint64_t end = min((c + 1) * CH16, n16);
         for (uint64_t i = c * CH16 + threadIdx.x; i < end; i += U * 256) {
-            uint4 v[U];
+            i32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) v[u] = i + u * 256 < end ? p[i + u * 256] : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < U; u++)
+                v[u] = i + u * 256 < end ? __builtin_nontemporal_load(p + i + u * 256) : (i32x4){0, 0, 0, 0};
 #pragma unroll
             for (int u = 0; u < U; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
         }
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(256) void mfma_fp8_kernel(int iters, float* sink)
 extern "C" int moe_probe_stream_read(const void* buf, size_t bytes, unsigned grid, uint32_t* sink, hipStream_t stream)
 {
     if (!buf || !sink || bytes < 16 || ((uintptr_t)buf & 15) || grid == 0) return 1;
-    stream_read_kernel<<<grid, 256, 0, stream>>>((const uint4*)buf, bytes / 16, sink);
+    stream_read_kernel<<<grid, 256, 0, stream>>>((const i32x4*)buf, bytes / 16, sink);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
