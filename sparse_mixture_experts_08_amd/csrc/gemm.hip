@@ -1284,8 +1284,11 @@ static void launch_f8(GemmArgs a, hipStream_t stream)
 }
 
 // 16-row tiles (bf16): output features per block, wavefronts, minimum wavefronts per SIMD.  inter and
-// inter_shared must be multiples of SMALL_UP_BN.
-static constexpr int SMALL_UP_BN = 64, SMALL_UP_WAVES = 4, SMALL_UP_MINW = 1;
+// inter_shared must be multiples of SMALL_UP_BN (the host requires multiples of 128).  The up GEMM's
+// 128-wide blocks of eight wavefronts stream W1 and W3 a little faster than 64-wide blocks of four
+// (64-token bf16 layer: 1.881 -> 1.852 ms, bitwise equal; 128 on four wavefronts 1.854, 256 on eight
+// 1.969); the down GEMM gains nothing from 128-wide blocks (0.962 -> 0.959 / 0.960 ms on four / eight).
+static constexpr int SMALL_UP_BN = 128, SMALL_UP_WAVES = 8, SMALL_UP_MINW = 1;
 static constexpr int SMALL_DN_BN = 64, SMALL_DN_WAVES = 4, SMALL_DN_MINW = 1;
 
 // Common fields of both GEMMs' arguments.
