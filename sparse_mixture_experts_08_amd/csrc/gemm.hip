@@ -882,13 +882,15 @@ __device__ __forceinline__ void mma_f8(const uint8_t* As_lds, const uint8_t* Bs_
         b1[j] = frag(Bs_lds, wn0 + j * 16 + r16);
         if constexpr (UP) b3[j] = frag(Bs_lds, BN + wn0 + j * 16 + r16);
     }
-    // The lane's WM row scales (rows wm0 + 16 i + r16) sit side by side in the stage's scale copy, so
-    // 16-byte reads at the start of the stage fetch them all.  A 4-byte read per row block, issued with
-    // the next A fragment, made each scale product wait for that fragment too (LDS reads complete in order).
+    // The lane's WM row scales (rows wm0 + 16 i + r16) sit in the stage's scale copy in groups of four
+    // (rows of blocks 4v .. 4v + 3 at wm0 + 64 v + 4 r16), so WM / 4 16-byte reads at the start of the
+    // stage fetch them all, the 16 lanes of a read covering 256 consecutive bytes (no bank conflicts).  A
+    // 4-byte read per row block, issued with the next A fragment, made each scale product wait for that
+    // fragment too (LDS reads complete in order).
     static_assert(WM % 4 == 0, "row scales as 16-byte vectors");
     f32x4 sv[WM / 4];
 #pragma unroll
-    for (int v = 0; v < WM / 4; v++) sv[v] = *(const f32x4*)(sA_lds + wm0 + r16 * WM + 4 * v);
+    for (int v = 0; v < WM / 4; v++) sv[v] = *(const f32x4*)(sA_lds + wm0 + 64 * v + 4 * r16);
     auto scale = [&](int i) { return sv[i >> 2][i & 3]; };   // row scale of the lane's token in row block i
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if constexpr (NB == 0) {
@@ -1130,9 +1132,10 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_f8_kernel(GemmArgs g)
     // scale copy of this wavefront: byte offset from its base, the base moved by the K stage below
     uint32_t soff = 0;
     if (wave < SW) {
-        // A row scales in the order mma_f8 reads them: position wm0 + WM r16 + i holds row wm0 + 16 i + r16
+        // A row scales in the order mma_f8 reads them: position wm0 + 64 v + 4 r16 + e holds row
+        // wm0 + 16 (4 v + e) + r16
         const int p = wave * 64 + lane, rem = p % (WM * 16);
-        soff = (uint32_t)s_tok[p - rem + (rem % WM) * 16 + rem / WM] * (uint32_t)g.ldas * 4u;
+        soff = (uint32_t)s_tok[p - rem + 16 * (4 * (rem / 64) + rem % 4) + (rem % 64) / 4] * (uint32_t)g.ldas * 4u;
     }
     else if (wave == SW || (UP && wave == SW + 1)) soff = (uint32_t)(lane < BN / 128 ? lane : 0) * (uint32_t)nkb * 4u;
 
