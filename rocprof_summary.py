@@ -78,15 +78,26 @@ COUNTER_PASSES = [
     "SQ_INSTS_MFMA",
     "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum TCP_PENDING_STALL_CYCLES_sum "
     "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_TOTAL_CACHE_ACCESSES_sum GRBM_GUI_ACTIVE",
+    "SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_WAIT_INST_LDS SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
+    "SQ_LDS_BANK_CONFLICT TA_BUSY_avr TA_ADDR_STALLED_BY_TC_CYCLES_sum GRBM_GUI_ACTIVE",
+    "TA_DATA_STALLED_BY_TC_CYCLES_sum TA_ADDR_STALLED_BY_TD_CYCLES_sum TD_TD_BUSY_sum TD_TC_STALL_sum "
+    "TCP_TCP_TA_DATA_STALL_CYCLES_sum TCP_TCR_TCP_STALL_CYCLES_sum TCP_PENDING_STALL_CYCLES_sum GRBM_GUI_ACTIVE "
+    "GRBM_COUNT",
 ]
 
 
 def counters_main(workload, dirs):
     vals = defaultdict(lambda: defaultdict(list))
-    for d in dirs:
+    # GRBM_GUI_ACTIVE is read in several passes; keep each pass's own value for the per-pass ratios below
+    gui = defaultdict(dict)
+    for i, d in enumerate(dirs):
         for r in _csv(d, "counter_collection.csv"):
             if "moe::" in r["Kernel_Name"]:
                 vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    gui[r["Kernel_Name"]].setdefault(i, []).append(float(r["Counter_Value"]))
+    gpu = max((r for d in dirs for r in _csv(d, "agent_info.csv")), key=lambda r: int(r.get("Num_Xcc") or 0))
+    nxcc, ncu = int(gpu["Num_Xcc"]), int(gpu["Cu_Count"])
     avg = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
     lines = [f"# rocprofv3 counters of the grouped GEMMs: {workload}", "",
              "Commands (run from /tmp with TMPDIR=/tmp on an MI355X; R = repository root, OUT = an output "
@@ -124,6 +135,29 @@ def counters_main(workload, dirs):
                      f"{fmt(None if lat is None or not req else lat / req, '{:.0f}')} | "
                      f"{fmt(None if wait is None or not wc else 100 * wait / wc)} | "
                      f"{fmt(None if iv is None or not im else iv / im, '{:.2f}')} |")
+    if len(dirs) >= 5:
+        lines += ["", "Vector-memory path (passes 4 and 5; per CU, as a fraction of the kernel's cycles = "
+                  f"GRBM_GUI_ACTIVE / {nxcc} XCDs, each pass against its own GRBM_GUI_ACTIVE; {ncu} CUs):", "",
+                  "- TD busy = TD_TD_BUSY / CUs; TD stalled by TC = TD_TC_STALL / CUs (the data-return unit waiting "
+                  "on the L1 / L2 for the next load's data); TA busy = TA_BUSY_avr; TA stalled by TC = "
+                  "TA_ADDR_STALLED_BY_TC_CYCLES / CUs; LDS indexed = SQ_LDS_IDX_ACTIVE / CUs (a sum over the SIMDs "
+                  "of each shader engine); LDS wait share = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES.", "",
+                  "| kernel | TD busy | TD stalled by TC | TA busy | TA stalled by TC | LDS indexed | "
+                  "LDS wait share |", "|---|---|---|---|---|---|---|"]
+        for k in sorted(avg, key=lambda k: -(g("GRBM_GUI_ACTIVE", k) or 0)):
+            c4 = sum(gui[k].get(3, [0])) / max(len(gui[k].get(3, [])), 1) / nxcc
+            c5 = sum(gui[k].get(4, [0])) / max(len(gui[k].get(4, [])), 1) / nxcc
+            if not c4 or not c5:
+                continue
+            td, tds = g("TD_TD_BUSY_sum", k), g("TD_TC_STALL_sum", k)
+            ta, tas = g("TA_BUSY_avr", k), g("TA_ADDR_STALLED_BY_TC_CYCLES_sum", k)
+            lds, wl, wc = g("SQ_LDS_IDX_ACTIVE", k), g("SQ_WAIT_INST_LDS", k), g("SQ_WAVE_CYCLES", k)
+            lines.append(f"| `{k}` | {fmt(None if td is None else td / ncu / c5, '{:.2f}')} | "
+                         f"{fmt(None if tds is None else tds / ncu / c5, '{:.2f}')} | "
+                         f"{fmt(None if ta is None else ta / c4, '{:.2f}')} | "
+                         f"{fmt(None if tas is None else tas / ncu / c4, '{:.2f}')} | "
+                         f"{fmt(None if lds is None else lds / ncu / c4, '{:.2f}')} | "
+                         f"{fmt(None if wl is None or not wc else wl / wc, '{:.3f}')} |")
     lines += ["", "Raw counter values (average per dispatch):", "", "| kernel | counter | value |", "|---|---|---|"]
     for k in sorted(avg):
         for c in sorted(avg[k]):
