@@ -33,7 +33,7 @@ from sparse_mixture_experts_08_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {W.BF16: 2500.0, W.FP8_E4M3: 5000.0, W.F32: 157.3}
-# fp32 vector peak without packed FMA (this build emits none): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+# fp32 vector peak without packed FMA (the kernels are compiled with packed fp32 ops off): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
 FP32_VALU_PEAK_TFLOPS = 78.6
 # the router's logit kernel: fp32 FMA chains on the vector ALU up to this many tokens, fp32 MFMA above
 ROUTER_FEW_MAX_T = 512

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
             for (int e = 0; e < 4; e++) {
                 const float a0 = acc[2 * e] + __uint_as_float(wv[e] << 16);
                 const float a1 = acc[2 * e + 1] + __uint_as_float(wv[e] & 0xFFFF0000u);
-                o[e] = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
+                o[e] = f32x2_to_bf16x2(a0, a1);
             }
         } else {
 #pragma unroll

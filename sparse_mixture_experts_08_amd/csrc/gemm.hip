@@ -199,7 +199,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, uint8_t* smem, 
             for (int j = 0; j < WN; j++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const float gg = round_bf16(acc1[i][j][r]), uu = round_bf16(acc3[i][j][r]);
+                    float gg = acc1[i][j][r], uu = acc3[i][j][r];
+                    round_bf16x2(gg, uu);
                     hs[(wm0 + i * 16 + 4 * q + r) * BN + wn0 + j * 16 + r16] = round_bf16(silu_mul_fast(gg, uu));
                 }
         __syncthreads();
@@ -806,17 +807,27 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
 
     // Epilogue (32x32 accumulator layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4):
     // the block's bf16 tile (UP: h = silu(g) * u, BN columns) into LDS, then coalesced to global memory.
+    // Rows come in pairs (r, r + 1 share a 4-row group), so one conversion rounds both outputs (and for UP
+    // one rounds g and u of each).
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
+        for (int r = 0; r < 16; r += 2) {
             const int row = wm0 + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
-                float v;
-                if constexpr (UP) v = silu_mul_fast(round_bf16(acc1[i][j][r]), round_bf16(acc3[i][j][r]));
-                else v = acc1[i][j][r];
-                *(uint16_t*)(ring + row * OSTR + (wn0 + 32 * j + r32) * 2) = f32_to_bf16(v);
+                float v0 = acc1[i][j][r], v1 = acc1[i][j][r + 1];
+                if constexpr (UP) {
+                    float u0 = acc3[i][j][r], u1 = acc3[i][j][r + 1];
+                    round_bf16x2(v0, u0);
+                    round_bf16x2(v1, u1);
+                    v0 = silu_mul_fast(v0, u0);
+                    v1 = silu_mul_fast(v1, u1);
+                }
+                const uint32_t p = f32x2_to_bf16x2(v0, v1);
+                uint8_t* o = ring + row * OSTR + (wn0 + 32 * j + r32) * 2;
+                *(uint16_t*)o = (uint16_t)p;
+                *(uint16_t*)(o + OSTR) = (uint16_t)(p >> 16);
             }
         }
     __syncthreads();
@@ -1010,10 +1021,17 @@ __device__ __forceinline__ void f8_epilogue(const GemmArgs& g, uint8_t* smem, co
             const int t = wm0 + i * 16 + r16;
 #pragma unroll
             for (int j = 0; j < WN; j++) {
-                f32x4 v;
+                float gv[4], uv[4];
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    v[r] = round_bf16(silu_mul_fast(round_bf16(acc1[i][j][r]), round_bf16(acc3[i][j][r])));
+                for (int r = 0; r < 4; r++) {
+                    gv[r] = acc1[i][j][r];
+                    uv[r] = acc3[i][j][r];
+                    round_bf16x2(gv[r], uv[r]);
+                    gv[r] = silu_mul_fast(gv[r], uv[r]);
+                }
+                round_bf16x2(gv[0], gv[1]);
+                round_bf16x2(gv[2], gv[3]);
+                const f32x4 v = {gv[0], gv[1], gv[2], gv[3]};
                 const int c = ((wn0 + j * 16) >> 2) + q;
                 *(f32x4*)(hs + t * BN + ((c ^ (t & 15)) << 2)) = v;
             }
@@ -1048,8 +1066,8 @@ __device__ __forceinline__ void f8_epilogue(const GemmArgs& g, uint8_t* smem, co
         for (int i = 0; i < WM; i++)
 #pragma unroll
             for (int j = 0; j < WN; j++) {
-                const uint32_t lo = (uint32_t)f32_to_bf16(acc1[i][j][0]) | ((uint32_t)f32_to_bf16(acc1[i][j][1]) << 16);
-                const uint32_t hi = (uint32_t)f32_to_bf16(acc1[i][j][2]) | ((uint32_t)f32_to_bf16(acc1[i][j][3]) << 16);
+                const uint32_t lo = f32x2_to_bf16x2(acc1[i][j][0], acc1[i][j][1]);
+                const uint32_t hi = f32x2_to_bf16x2(acc1[i][j][2], acc1[i][j][3]);
                 *(uint2*)(smem + (wm0 + i * 16 + r16) * OSTR + (wn0 + j * 16 + 4 * q) * 2) = make_uint2(lo, hi);
             }
         __syncthreads();

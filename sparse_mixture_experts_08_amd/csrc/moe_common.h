@@ -15,16 +15,30 @@ namespace moe {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to the nearest bf16 (ties to even) and return its bit pattern.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+// Two floats rounded to the nearest bf16 (ties to even) by the hardware conversion (v_cvt_pk_bf16_f32:
+// one instruction for both, against three integer operations each for the same rounding done on the bit
+// pattern), packed as a | b << 16.  For every finite float, subnormals included, it gives the bit pattern
+// of u + 0x7FFF + (u >> 16 & 1), shifted right by 16; NaNs stay NaNs.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
+
+// Round to the nearest bf16 (ties to even) and return its bit pattern.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.f); }
 
 // Round to the nearest bf16 (ties to even), returned as the (exact) float value.
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// a and b rounded to the nearest bf16 in place, by one conversion.
+__device__ __forceinline__ void round_bf16x2(float& a, float& b)
+{
+    const uint32_t p = f32x2_to_bf16x2(a, b);
+    a = __uint_as_float(p << 16);
+    b = __uint_as_float(p & 0xFFFF0000u);
+}
 
 // Value rounded to the activation dtype (fp32: identity).
 template <bool ACT_BF16>
