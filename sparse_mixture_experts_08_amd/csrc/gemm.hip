@@ -569,16 +569,25 @@ __device__ __forceinline__ bool block_work(const GemmArgs& g, int& tile, int& nb
 // Coalesced store of a block's bf16 output tile: the wavefronts have written it row-major into LDS (row
 // stride OSTR bytes, padded so the two row groups of one LDS write fall on different banks); every
 // thread then copies 16-byte chunks of rows < rows to out (row0 + row, col0 ..), ldo elements apart.
-// Against per-lane 2-byte global stores straight from the accumulators this writes whole lines.
-template <int BM, int OC, int OSTR, int NT>
+// Against per-lane 2-byte global stores straight from the accumulators this writes whole lines (and
+// against 8-byte stores straight from the fp8 kernel's accumulators, 32 contiguous bytes a row: fp8 down
+// GEMM 4.83 -> 5.35 ms).  NTS: stores with the non-temporal hint, for the down GEMMs' expert-output rows,
+// which only the combine reads, after the whole GEMM (prefill down GEMM 1.795 -> 1.695 ms, fp8 down GEMM
+// 4.77 -> 4.68 ms, skewed down GEMM 0.3 % slower).
+template <int BM, int OC, int OSTR, int NT, bool NTS = false>
 __device__ __forceinline__ void store_tile_bf16(const uint8_t* tile, uint8_t* out, int64_t ldo, int row0, int rows,
                                                 int col0)
 {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     constexpr int CH = OC * 2 / 16;                    // 16-byte chunks per row
     for (int idx = threadIdx.x; idx < BM * CH; idx += NT) {
         const int row = idx / CH, ch = idx % CH;
-        if (row < rows)
-            *(uint4*)(out + (((int64_t)row0 + row) * ldo + col0 + ch * 8) * 2) = *(const uint4*)(tile + row * OSTR + ch * 16);
+        if (row < rows) {
+            u32x4_t* dst = (u32x4_t*)(out + (((int64_t)row0 + row) * ldo + col0 + ch * 8) * 2);
+            const u32x4_t v = *(const u32x4_t*)(tile + row * OSTR + ch * 16);
+            if constexpr (NTS) __builtin_nontemporal_store(v, dst);
+            else *dst = v;
+        }
     }
 }
 
@@ -831,7 +840,7 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_w_kernel(GemmArgs g)
             }
         }
     __syncthreads();
-    store_tile_bf16<BM, BN, OSTR, 64 * NW>(ring, g.out, g.ldo, row0, rows, n0);
+    store_tile_bf16<BM, BN, OSTR, 64 * NW, !UP>(ring, g.out, g.ldo, row0, rows, n0);
 }
 
 // One 128-wide K stage of fp8 MFMAs for the direct-to-LDS fp8 kernel: the wavefront's WM x WN blocks of
@@ -1071,7 +1080,7 @@ __device__ __forceinline__ void f8_epilogue(const GemmArgs& g, uint8_t* smem, co
                 *(uint2*)(smem + (wm0 + i * 16 + r16) * OSTR + (wn0 + j * 16 + 4 * q) * 2) = make_uint2(lo, hi);
             }
         __syncthreads();
-        store_tile_bf16<BM, BN, OSTR, NT>(smem, g.out, g.ldo, row0, rows, n0);
+        store_tile_bf16<BM, BN, OSTR, NT, true>(smem, g.out, g.ldo, row0, rows, n0);
     }
 }
 
