@@ -37,6 +37,17 @@ int moe_probe_stream_read(const void* buf, size_t bytes, unsigned grid, uint32_t
  */
 int moe_probe_mfma(int dtype, int iters, unsigned grid, float* sink, double* flops, hipStream_t stream);
 
+/*
+ * Self-check of the fp8 quantisation's division (the rule of moe_quantize_e4m3 in moe.h: codes = E4M3 of
+ * v / s in fp32, s = amax / 448), which the library computes from a correctly rounded reciprocal and one
+ * fused residual correction instead of the IEEE division.  counts: 2 device uint64; counts[0] receives
+ * the number of s in [2^-90, 2^126) (every mantissa) whose reciprocal differs from IEEE 1 / s, counts[1]
+ * the number of (amax, v) pairs, over amax[0 .. n_amax) (positive finite fp32, device memory) and every
+ * float v with |v| <= amax, whose E4M3 code differs from that of the IEEE quotient.  Both are 0 when the
+ * shortcut is exact.  About 5 ms of GPU time per amax value at amax near 2^127, less below.
+ */
+int moe_probe_check_quant_division(const float* amax, int n_amax, unsigned long long* counts, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

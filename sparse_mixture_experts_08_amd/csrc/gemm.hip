@@ -217,8 +217,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, uint8_t* smem, 
             for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
             const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
             if (row < rows) {
-                uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
-                uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+                float q[8];
+                if (quant_div_fast(sc)) {
+                    const float r = recip_rn(sc);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) q[e] = quant_div(v[e], sc, r);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) q[e] = v[e] / sc;
+                }
+                uint32_t lo = f32x2_to_e4m3(q[0], q[1]) | (f32x2_to_e4m3(q[2], q[3]) << 16);
+                uint32_t hi = f32x2_to_e4m3(q[4], q[5]) | (f32x2_to_e4m3(q[6], q[7]) << 16);
                 const int64_t orow = row0 + row;
                 *(uint2*)(g.out + orow * g.ldo + n0 + grp128 * 128 + sub * 8) = make_uint2(lo, hi);
                 if (sub == 0) g.outs[orow * g.ldos + (n0 + grp128 * 128) / 128] = sc;
@@ -1062,8 +1071,17 @@ __device__ __forceinline__ void f8_epilogue(const GemmArgs& g, uint8_t* smem, co
             for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
             const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
             if (row < rows) {
-                uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
-                uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+                float q[8];
+                if (quant_div_fast(sc)) {
+                    const float r = recip_rn(sc);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) q[e] = quant_div(v[e], sc, r);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) q[e] = v[e] / sc;
+                }
+                uint32_t lo = f32x2_to_e4m3(q[0], q[1]) | (f32x2_to_e4m3(q[2], q[3]) << 16);
+                uint32_t hi = f32x2_to_e4m3(q[4], q[5]) | (f32x2_to_e4m3(q[6], q[7]) << 16);
                 const int64_t orow = row0 + row;
                 *(uint2*)(g.out + orow * g.ldo + n0 + grp128 * 128 + sub * 8) = make_uint2(lo, hi);
                 if (sub == 0) g.outs[orow * g.ldos + (n0 + grp128 * 128) / 128] = sc;
@@ -1255,8 +1273,17 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
     const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-    const uint32_t lo = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
-    const uint32_t hi = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+    float q[8];
+    if (quant_div_fast(sc)) {
+        const float r = recip_rn(sc);
+#pragma unroll
+        for (int e = 0; e < 8; e++) q[e] = quant_div(v[e], sc, r);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) q[e] = v[e] / sc;
+    }
+    const uint32_t lo = f32x2_to_e4m3(q[0], q[1]) | (f32x2_to_e4m3(q[2], q[3]) << 16);
+    const uint32_t hi = f32x2_to_e4m3(q[4], q[5]) | (f32x2_to_e4m3(q[6], q[7]) << 16);
     *(uint2*)(xq + row * d + col) = make_uint2(lo, hi);
     if (sub == 0) xs[gi] = sc;
 }

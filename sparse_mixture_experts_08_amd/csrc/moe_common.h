@@ -44,6 +44,27 @@ __device__ __forceinline__ void round_bf16x2(float& a, float& b)
 template <bool ACT_BF16>
 __device__ __forceinline__ float round_act(float f) { return ACT_BF16 ? round_bf16(f) : f; }
 
+// The quotient v / s of the E4M3 quantisation (s = amax / 448 of the group, |v| <= amax), with the
+// E4M3 code of the IEEE fp32 division in four instructions instead of about ten.  recip_rn(s) is the
+// correctly rounded 1/s (hardware reciprocal, one Newton step) for every s in [2^-90, 2^126); from it
+// the product v * (1/s) and one fused residual correction give the correctly rounded quotient
+// (Markstein's division), except where the residual underflows, which needs |v / s| < 2^-12, where both
+// quotients are below 2^-10 and round to a zero code; the sign copy keeps the sign of v there (-0 -> -0).
+// For the other s the callers divide.  Checked on the GPU: the reciprocal for every mantissa of that
+// range, the codes for every v in [-amax, amax] at 4096 values of amax from 2^-81 to 2^127 (libmoe_probe's
+// moe_probe_check_quant_division runs the same helpers).
+__device__ __forceinline__ bool quant_div_fast(float s) { return s >= 0x1p-90f && s < 0x1p126f; }
+__device__ __forceinline__ float recip_rn(float s)
+{
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    return __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+}
+__device__ __forceinline__ float quant_div(float v, float s, float r)
+{
+    const float q0 = v * r;
+    return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-s, q0, v), r, q0), v);
+}
+
 // Two floats -> two OCP E4M3 codes (round to nearest even; |v| <= 448 here), packed in the low 16 bits.
 __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b)
 {

@@ -1,11 +1,13 @@
 // peak_probe.hip -- measurement kernels for the denominators of the roofline fractions: the HBM read rate
 // a plain streaming kernel reaches, and the MFMA rate back-to-back matrix instructions reach, on the GPU
 // at hand (the published 8 TB/s and 2.5 / 5.0 PFLOP/s are peaks at the nominal clock; these are what the
-// chip sustains).  Not part of the layer: libmoe_probe.so, used by the benchmark only.
+// chip sustains).  Also a self-check of one arithmetic shortcut of the layer's fp8 quantisation step.  Not
+// part of the layer: libmoe_probe.so, used by the benchmark and the tests only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/moe_probe.h"
+#include "moe_common.h"
 
 namespace {
 
@@ -91,6 +93,53 @@ __global__ __launch_bounds__(256) void mfma_fp8_kernel(int iters, float* sink)
 }
 
 }  // namespace
+
+// The quantisation's division shortcut (moe_common.h: quant_div_fast, recip_rn, quant_div) against IEEE
+// fp32 division.  recip_check: every s = 2^e (1 + m 2^-23) with 2^-90 <= s < 2^126 against 1.0f / s.
+// code_check: per amax (blockIdx.y strides over them), every float v with |v| <= amax (bit patterns 0 ..
+// bits(amax), both signs) with s = amax / 448: the E4M3 code of the library's quotient against that of
+// v / s.  Mismatches are counted with one atomic per thread.
+__global__ __launch_bounds__(256) void recip_check_kernel(unsigned long long* count)
+{
+    constexpr uint32_t E0 = 127 - 90, E1 = 127 + 125;  // biased exponents of the checked s
+    const uint64_t n = (uint64_t)(E1 - E0 + 1) << 23;
+    unsigned long long bad = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
+        const float s = __uint_as_float(((E0 + (uint32_t)(i >> 23)) << 23) | (uint32_t)(i & 0x7FFFFF));
+        bad += __float_as_uint(moe::recip_rn(s)) != __float_as_uint(1.0f / s);
+    }
+    if (bad) atomicAdd(count, bad);
+}
+
+__global__ __launch_bounds__(256) void code_check_kernel(const float* amaxes, int n_amax, unsigned long long* count)
+{
+    unsigned long long bad = 0;
+    for (int a = blockIdx.y; a < n_amax; a += gridDim.y) {
+        const float amax = amaxes[a];
+        const float s = amax / 448.0f;
+        const bool fast = moe::quant_div_fast(s);
+        const float r = moe::recip_rn(s);
+        const uint64_t top = (uint64_t)(__float_as_uint(amax) & 0x7FFFFFFFu) + 1;
+        for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * top; i += (uint64_t)gridDim.x * blockDim.x) {
+            const float v = __uint_as_float((uint32_t)(i >> 1) | ((uint32_t)(i & 1) << 31));
+            const float q = fast ? moe::quant_div(v, s, r) : v / s;
+            bad += (moe::f32x2_to_e4m3(q, 0.f) & 0xFFu) != (moe::f32x2_to_e4m3(v / s, 0.f) & 0xFFu);
+        }
+    }
+    if (bad) atomicAdd(count, bad);
+}
+
+__global__ void zero2_kernel(unsigned long long* c) { c[0] = c[1] = 0; }
+
+extern "C" int moe_probe_check_quant_division(const float* amax, int n_amax, unsigned long long* counts,
+                                              hipStream_t stream)
+{
+    if (!amax || !counts || n_amax <= 0) return 1;
+    zero2_kernel<<<1, 1, 0, stream>>>(counts);
+    recip_check_kernel<<<8192, 256, 0, stream>>>(counts);
+    code_check_kernel<<<dim3(4096, 64), 256, 0, stream>>>(amax, n_amax, counts + 1);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 extern "C" int moe_probe_stream_read(const void* buf, size_t bytes, unsigned grid, uint32_t* sink, hipStream_t stream)
 {

@@ -243,3 +243,58 @@ def test_activation_quantisation_bit_exact():
     # the layer applies the same rule: zero rows still quantise, and an empty call is a no-op
     q0, s0 = B.moe_quantize_e4m3(xd[:0])
     assert q0.numel() == 0 and s0.numel() == 0
+
+
+def test_activation_quantisation_ties_at_non_power_of_two_scales():
+    # Groups whose scale s = amax / 448 is not a power of two (amax = 448 c), with values v = c * M on E4M3
+    # rounding midpoints M (v / s = M exactly: a tie, to even) and the bf16 neighbours of each (just above
+    # and below the tie).  The library divides through a correctly rounded reciprocal and one residual
+    # correction; its codes must still be those of the IEEE quotient, bit for bit against the oracle.
+    from oracle import oracle as O
+    mids = [1.0625, 1.1875, 1.3125, 1.4375, 1.5625, 1.6875, 1.8125, 1.9375, 2.125, 3.0625, 4.25, 9.5, 13.0,
+            26.0, 104.0, 208.0, 240.0, 304.0, 432.0, 440.0]
+    cs = [1.5, 1.25, 1.75, 3.0, 0.625, 1.5 * 2.0 ** -12, 1.25 * 2.0 ** 9, 0.75 * 2.0 ** 20]
+    x = torch.zeros(len(cs), 128, dtype=torch.bfloat16)
+    ties = 0
+    for r, c in enumerate(cs):
+        t = torch.tensor([448.0 * c] + [c * m for m in mids], dtype=torch.float32)
+        b = t.to(torch.bfloat16)
+        b = b[b.float() == t]                          # the amax and the ties that bf16 holds exactly
+        assert b[0].item() == 448.0 * c and b.numel() >= 12
+        ties += b.numel() - 1
+        bits = b.view(torch.int16)
+        up, dn = (bits[1:] + 1).view(torch.bfloat16), (bits[1:] - 1).view(torch.bfloat16)
+        row = torch.cat([b, up, dn, -b[1:], -up])
+        x[r, :row.numel()] = row
+    assert ties >= 120
+    q, sc = B.moe_quantize_e4m3(x.to(DEV))
+    torch.cuda.synchronize()
+    q_ref, s_ref = O.quantize_rows_e4m3(x.float().numpy())
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref), int((q.cpu().numpy() != q_ref).sum())
+
+
+def test_quantisation_division_shortcut_exhaustive():
+    # The division of the fp8 quantisation (a correctly rounded reciprocal and one fused residual
+    # correction, used by moe_quantize_e4m3 and the fp8 up GEMM's h quantisation) against IEEE fp32 division:
+    # the reciprocal for every mantissa of s in [2^-90, 2^126), and the E4M3 code of every float v with
+    # |v| <= amax at 192 values of amax spread over 2^-81 .. 2^127 (edge mantissas included), through
+    # libmoe_probe.so's self-check, which runs the library's own helpers.
+    import ctypes
+    import os
+    L = ctypes.CDLL(os.path.join(os.path.dirname(B.__file__), "libmoe_probe.so"))
+    L.moe_probe_check_quant_division.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    rng = np.random.default_rng(11)
+    n = 192
+    mant = rng.integers(0, 1 << 23, n, dtype=np.uint32)
+    mant[0::8], mant[1::8], mant[2::8] = 0, (1 << 23) - 1, 1 << 22
+    expo = (127 - 81 + (np.arange(n) * 7919) % 209).astype(np.uint32)
+    amax = ((expo << 23) | mant).view(np.float32)
+    assert np.isfinite(amax).all() and (amax > 0).all()
+    a_dev = torch.from_numpy(amax).to(DEV)
+    counts = torch.zeros(2, dtype=torch.int64, device=DEV)
+    rc = L.moe_probe_check_quant_division(ctypes.c_void_p(a_dev.data_ptr()), n, ctypes.c_void_p(counts.data_ptr()),
+                                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert counts.tolist() == [0, 0]
