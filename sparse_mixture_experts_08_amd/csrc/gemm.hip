@@ -213,8 +213,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, uint8_t* smem, 
             float amax = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+            amax = row16_max(amax);
             const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
             if (row < rows) {
                 float q[8];
@@ -1067,8 +1066,7 @@ __device__ __forceinline__ void f8_epilogue(const GemmArgs& g, uint8_t* smem, co
             float amax = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+            amax = row16_max(amax);
             const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
             if (row < rows) {
                 float q[8];
@@ -1270,8 +1268,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    amax = row16_max(amax);
     const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
     float q[8];
     if (quant_div_fast(sc)) {

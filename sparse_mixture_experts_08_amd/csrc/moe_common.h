@@ -65,6 +65,25 @@ __device__ __forceinline__ float quant_div(float v, float s, float r)
     return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-s, q0, v), r, q0), v);
 }
 
+// Maximum of a non-negative, non-NaN x over each aligned group of 16 lanes (a DPP row), returned to every
+// lane of the group: four DPP moves (the neighbour in a pair, the other pair of a quad, the mirrored quad
+// of a half-row, the mirrored half-row) instead of four LDS permutes.  Such floats order as their bit
+// patterns do, so the maxima are integer maxima (no NaN canonicalisation).  Every lane of a group must be
+// active.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row16_max(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    u = max(u, dpp_u32<0xB1>(u));                      // quad_perm [1, 0, 3, 2]
+    u = max(u, dpp_u32<0x4E>(u));                      // quad_perm [2, 3, 0, 1]
+    u = max(u, dpp_u32<0x141>(u));                     // row_half_mirror
+    u = max(u, dpp_u32<0x140>(u));                     // row_mirror
+    return __uint_as_float(u);
+}
+
 // Two floats -> two OCP E4M3 codes (round to nearest even; |v| <= 448 here), packed in the low 16 bits.
 __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b)
 {
