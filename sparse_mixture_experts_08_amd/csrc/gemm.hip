@@ -270,6 +270,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
     constexpr int KE = 128 / Elem<ET>::bytes;          // K elements per stage
     constexpr bool FP8 = ET == ET_FP8;
     static_assert((WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8) && WM >= 1 && WN >= 1, "4 or 8 waves");
+    static_assert(NBUF == 1 || NBUF == 2, "single- or double-buffered stages (the loop below knows no other)");
     static_assert(BM <= NT, "one thread per tile row for the row tables");
     static_assert(!FP8 || (WN * 16 <= 128 && 128 % (WN * 16) == 0), "a wavefront's columns share one fp8 block scale");
     static_assert(!(FP8 && UP) || BN % 128 == 0, "fp8 h quantisation needs whole 128-column groups");
