@@ -1,7 +1,8 @@
 /*
  * moe_probe.h -- measurement kernels of libmoe_probe.so, used by the benchmark to state each roofline
- * fraction against what this GPU sustains as well as against its published peaks.  They are not part of
- * the layer (moe.h); they compute nothing of it.  The HBM ceiling they measure is the one the pages say
+ * fraction against what this GPU sustains as well as against its published peaks, and one self-check of an
+ * arithmetic shortcut the layer takes (used by the tests).  They are not part of the layer (moe.h); they
+ * compute nothing of it.  The HBM ceiling they measure is the one the pages say
  * decides serving ("DeepSeek-V3's mixture-of-experts architecture explained", "Inference reality check":
  * loading the experts' weights dominates), the MFMA one the ceiling of the expert GEMMs at large batch.
  * Conventions as in moe.h: device pointers, work enqueued on `stream`, no host synchronisation; return 0
