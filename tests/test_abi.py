@@ -32,6 +32,21 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+PROBE_HEADER = os.path.join(ROOT, "include", "moe_probe.h")
+PROBE_LIB = os.path.join(os.path.dirname(B.LIB_PATH), "libmoe_probe.so")
+
+
+@pytest.mark.skipif(not os.path.exists(PROBE_LIB), reason="libmoe_probe.so not built")
+def test_probe_library_exports_every_declared_symbol():
+    # the measurement library of include/moe_probe.h (peaks, the quantisation self-check) likewise
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_probe_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["moe_probe_check_quant_division", "moe_probe_mfma", "moe_probe_stream_read"]
+    L = ctypes.CDLL(PROBE_LIB, mode=os.RTLD_NOW)
+    for name in names:
+        assert hasattr(L, name), name
+
+
 def _shape(**kw):
     base = dict(T=64, d=7168, E=256, k=8, inter=2048, inter_shared=2048, act_dtype=B.MOE_BF16, w_dtype=B.MOE_BF16)
     base.update(kw)
