@@ -257,6 +257,43 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, uint8_t* smem, 
     }
 }
 
+// block -> (tile, n-block); false when the block has no work.  group_m == 0 (decode-sized tiles):
+// consecutive blocks walk one tile's n-blocks.  Otherwise the work list is cut into groups of group_m
+// consecutive tiles x all n-blocks, walked n-block by n-block with the group's tiles fastest, and the
+// groups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8; XCD x takes groups x, x + 8,
+// x + 16, ..., one after the other).  Blocks that run together on one XCD share A rows (same tile) and
+// weight panels (same expert, n-block) in that XCD's L2, and every XCD gets a like share of hot, cold and
+// shared-expert tiles: cut into 8 contiguous ranges instead, the list gave one XCD all 16 shared tiles of
+// the 4096-token layer (about a quarter more work than the others) and the skewed layer's XCDs 5-6 % more
+// or less than their mean.  launch_blocks() is the grid this needs.
+__device__ __forceinline__ bool block_work(const GemmArgs& g, int& tile, int& nb)
+{
+    const int bid = blockIdx.x;
+    const int nt = *g.ntiles;
+    if (g.group_m == 0) {
+        tile = bid / g.n_blocks;
+        nb = bid % g.n_blocks;
+        return tile < nt;
+    }
+    const int items = g.group_m * g.n_blocks;          // work items of a full group
+    const int j = bid >> 3;                            // the block's place in its XCD's list
+    const int c = (bid & 7) + 8 * (j / items), r = j % items;
+    if (c * g.group_m >= nt) return false;
+    const int gm = min(g.group_m, nt - c * g.group_m); // the last group may be short
+    if (r >= gm * g.n_blocks) return false;
+    nb = r / gm;
+    tile = c * g.group_m + r % gm;
+    return true;
+}
+
+// Grid of a grouped-GEMM launch: enough blocks for max_tiles tiles under block_work's mapping.
+static int64_t launch_blocks(const GemmArgs& a)
+{
+    if (a.group_m == 0) return ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
+    const int64_t groups = (a.max_tiles + a.group_m - 1) / a.group_m;
+    return 8 * ((groups + 7) / 8) * a.group_m * a.n_blocks;
+}
+
 // NBUF: LDS stages (2 = double buffered, one barrier per K stage; 1 = single buffer, two barriers per
 // stage but half the LDS, so two blocks share a CU and cover each other's barriers).  MINW: minimum
 // wavefronts per SIMD the register allocation must allow.
@@ -280,31 +317,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void grouped_gemm_ker
     __shared__ float sA[NBUF][BM];
     __shared__ int s_tok[BM];
 
-    // block -> (tile, n-block).  Decode-sized tiles: consecutive blocks walk one tile's n-blocks.
-    // Otherwise blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8), so the
-    // work list (tile, n-block) is cut into 8 contiguous ranges, one per XCD, and inside a range the
-    // items go group by group: group_m consecutive tiles x all n-blocks, tiles fastest.  Blocks that run
-    // together on one XCD then share A rows (same tile) and weight panels (same expert, n-block) in
-    // that XCD's L2.
-    const int bid = blockIdx.x;
     int tile, nb;
-    if (g.group_m == 0) {
-        tile = bid / g.n_blocks;
-        nb = bid % g.n_blocks;
-        if (tile >= *g.ntiles) return;
-    } else {
-        const int nt = *g.ntiles;
-        const int total = nt * g.n_blocks;
-        const int per = (total + 7) / 8;
-        if (bid >= 8 * per) return;
-        const int l = (bid & 7) * per + (bid >> 3);
-        if (l >= total) return;
-        const int items = g.group_m * g.n_blocks;
-        const int c = l / items, r = l % items;
-        const int gm = min(g.group_m, nt - c * g.group_m);
-        nb = r / gm;
-        tile = c * g.group_m + r % gm;
-    }
+    if (!block_work(g, tile, nb)) return;
     const int4 td = g.tiles[tile];
     const int grp = td.x, row0 = td.y, rows = td.z;
     const bool shared = grp == g.E;
@@ -551,29 +565,6 @@ __device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32
                  : "m0");
 }
 #pragma clang diagnostic pop
-
-// block -> (tile, n-block), the same mapping as grouped_gemm_kernel; false when the block has no work.
-__device__ __forceinline__ bool block_work(const GemmArgs& g, int& tile, int& nb)
-{
-    const int bid = blockIdx.x;
-    if (g.group_m == 0) {
-        tile = bid / g.n_blocks;
-        nb = bid % g.n_blocks;
-        return tile < *g.ntiles;
-    }
-    const int nt = *g.ntiles;
-    const int total = nt * g.n_blocks;
-    const int per = (total + 7) / 8;
-    if (bid >= 8 * per) return false;
-    const int l = (bid & 7) * per + (bid >> 3);
-    if (l >= total) return false;
-    const int items = g.group_m * g.n_blocks;
-    const int c = l / items, r = l % items;
-    const int gm = min(g.group_m, nt - c * g.group_m);
-    nb = r / gm;
-    tile = c * g.group_m + r % gm;
-    return true;
-}
 
 // Coalesced store of a block's bf16 output tile: the wavefronts have written it row-major into LDS (row
 // stride OSTR bytes, padded so the two row groups of one LDS write fall on different banks); every
@@ -1301,7 +1292,7 @@ hipError_t launch_act_quant(const moe_shape_t& s, const void* x, const Workspace
 template <int ET, bool UP, bool ACT_BF16, int BM, int BN, int WAVES_M, int WAVES_N, int NBUF = 2, int MINW = 1>
 static void launch_one(GemmArgs a, hipStream_t stream)
 {
-    const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
+    const int64_t nblk = launch_blocks(a);
     grouped_gemm_kernel<ET, UP, ACT_BF16, BM, BN, WAVES_M, WAVES_N, NBUF, MINW>
         <<<(unsigned)nblk, 64 * WAVES_M * WAVES_N, 0, stream>>>(a);
 }
@@ -1312,11 +1303,12 @@ static constexpr int KROT_UP16 = 0;
 static constexpr int KROT_UP = 3;
 static constexpr int KROT_WDN = 3;   // wide-kernel down GEMM (rotations 0 / 1 / 5 / 7 / 13 measured slower)
 static constexpr int KROT_DN = 1;
-// Tiles per XCD group of the large-tile block order (see grouped_gemm_kernel).  The fp8 down GEMM, whose
-// h rows are short (inter bytes) and whose 256-wide n-blocks are many (d / 256), does best with groups of
-// two tiles (32768-token fp8 layer: 1 / 2 / 3 / 8 tiles 5.11 / 5.08 / 5.11 / 5.31 ms, bitwise equal); the
-// bf16 down GEMM does not (skewed 4.50 -> 4.66 ms with two).
-static constexpr int GROUP_M = 8;
+// Tiles per group of the large-tile block order (block_work: groups dealt round-robin to the XCDs).
+// Four for the GEMMs in general (skewed layer, groups of 2 / 3 / 4 / 6 / 8 tiles: 13.66 / 13.64 / 13.56 /
+// 13.79 / 13.82 ms; fp8 layer 4 / 8 / 16: 16.15 / 16.14 / 16.29 ms; all bitwise equal); the fp8 down GEMM,
+// whose h rows are short (inter bytes) and whose 256-wide n-blocks are many (d / 256), does best with
+// groups of two (fp8 layer, down GEMM with 1 / 2 / 4: 4.70 / 4.67 / 4.76 ms).
+static constexpr int GROUP_M = 4;
 static constexpr int GROUP_M_F8_DN = 2;
 
 // bf16 256-row tiles: 128-byte K stages in a ring of two (64-byte stages in deeper rings request twice
@@ -1326,7 +1318,7 @@ static constexpr int GROUP_M_F8_DN = 2;
 template <bool UP>
 static void launch_w(GemmArgs a, hipStream_t stream)
 {
-    const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
+    const int64_t nblk = launch_blocks(a);
     grouped_gemm_w_kernel<UP, 256, 128, 2, 3, 8><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
 
@@ -1334,7 +1326,7 @@ static void launch_w(GemmArgs a, hipStream_t stream)
 template <bool UP, int BM, int BN>
 static void launch_f8(GemmArgs a, hipStream_t stream)
 {
-    const int64_t nblk = ((int64_t)a.n_blocks * a.max_tiles + 7) / 8 * 8;
+    const int64_t nblk = launch_blocks(a);
     grouped_gemm_f8_kernel<UP, BM, BN, BM == 128 ? 3 : 2><<<(unsigned)nblk, 512, 0, stream>>>(a);
 }
 
