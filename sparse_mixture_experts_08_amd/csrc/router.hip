@@ -79,7 +79,13 @@ struct W4 {
 // step of i).  Block = 4 wavefronts x 16 tokens = 64 tokens, x 64 NS experts; K staged through
 // double-buffered LDS 32 at a time ([t][i] and [e][i] rows padded to 144 bytes, so 16 lanes reading
 // 16 B each hit distinct banks), global loads two stages ahead as in the kernels above.
-template <typename XT, int NS>
+// FLAT: the stage loop walks whole pairs of stages with an odd last stage after it, which keeps the
+// accumulators in one register range (the form with a break inside the pair copies them between two
+// ranges every pair: 32 extra moves per 64 MFMAs).  With four or more wavefronts per SIMD (above 8192
+// tokens) that is faster (16384 / 32768 tokens: 0.683 -> 0.662 / 1.219 -> 1.178 ms, logits bitwise
+// equal); with one (4096 tokens) the compiler's schedule of the other form hides the LDS reads better
+// (0.225 against 0.261 ms).
+template <typename XT, int NS, bool FLAT>
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
                                                                 const float* __restrict__ bias, float* __restrict__ L,
                                                                 int T, int d, int E)
@@ -141,18 +147,35 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const XT* __res
     if (ns > 1) load(rb, BK);
     store(ra, 0);
     __syncthreads();
-    for (int s = 0; s < ns; s += 2) {
-        // stage s is in LDS buffer 0; rb holds stage s + 1 (in flight)
-        if (s + 2 < ns) load(ra, (s + 2) * BK);
-        compute(0);
-        if (s + 1 >= ns) break;
-        store(rb, 1);
-        __syncthreads();
-        // stage s + 1 is in LDS buffer 1; ra holds stage s + 2 (in flight)
-        if (s + 3 < ns) load(rb, (s + 3) * BK);
-        compute(1);
-        if (s + 2 < ns) store(ra, 0);
-        __syncthreads();
+    if constexpr (FLAT) {
+        int s = 0;
+        for (; s + 1 < ns; s += 2) {
+            // stage s is in LDS buffer 0; rb holds stage s + 1 (in flight)
+            if (s + 2 < ns) load(ra, (s + 2) * BK);
+            compute(0);
+            store(rb, 1);
+            __syncthreads();
+            // stage s + 1 is in LDS buffer 1; ra holds stage s + 2 (in flight)
+            if (s + 3 < ns) load(rb, (s + 3) * BK);
+            compute(1);
+            if (s + 2 < ns) store(ra, 0);
+            __syncthreads();
+        }
+        if (s < ns) compute(0);                        // an odd stage count: the last stage, in buffer 0
+    } else {
+        for (int s = 0; s < ns; s += 2) {
+            // stage s is in LDS buffer 0; rb holds stage s + 1 (in flight)
+            if (s + 2 < ns) load(ra, (s + 2) * BK);
+            compute(0);
+            if (s + 1 >= ns) break;
+            store(rb, 1);
+            __syncthreads();
+            // stage s + 1 is in LDS buffer 1; ra holds stage s + 2 (in flight)
+            if (s + 3 < ns) load(rb, (s + 3) * BK);
+            compute(1);
+            if (s + 2 < ns) store(ra, 0);
+            __syncthreads();
+        }
     }
 #pragma unroll
     for (int s = 0; s < NS; s++)
@@ -295,6 +318,8 @@ static void launch_few(dim3 grid, const XT* x, const float* Wg, const float* bia
 // and DPP row-rotation kernels it replaces, routing bitwise equal).
 static constexpr int ROUTER_FEW_MAX_T = 512;
 static constexpr int ROUTER_MFMA_NS = 1;
+// Above this many tokens the MFMA logit kernel takes its FLAT stage loop (four or more wavefronts per SIMD).
+static constexpr int64_t ROUTER_FLAT_MIN_T = 8192;
 
 hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float* Wg, const float* bias,
                                 float* logits, hipStream_t stream)
@@ -312,12 +337,17 @@ hipError_t launch_router_logits(const moe_shape_t& s, const void* x, const float
         else launch_few<float, 16>(grid, (const float*)x, Wg, bias, logits, T, d, E, stream);
     } else {
         dim3 grid((E + 64 * ROUTER_MFMA_NS - 1) / (64 * ROUTER_MFMA_NS), (T + 63) / 64);
+        const bool flat = T > ROUTER_FLAT_MIN_T;
         if (bf)
-            router_logits_mfma_kernel<uint16_t, ROUTER_MFMA_NS>
-                <<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
+            flat ? router_logits_mfma_kernel<uint16_t, ROUTER_MFMA_NS, true>
+                       <<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E)
+                 : router_logits_mfma_kernel<uint16_t, ROUTER_MFMA_NS, false>
+                       <<<grid, 256, 0, stream>>>((const uint16_t*)x, Wg, bias, logits, T, d, E);
         else
-            router_logits_mfma_kernel<float, ROUTER_MFMA_NS>
-                <<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
+            flat ? router_logits_mfma_kernel<float, ROUTER_MFMA_NS, true>
+                       <<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E)
+                 : router_logits_mfma_kernel<float, ROUTER_MFMA_NS, false>
+                       <<<grid, 256, 0, stream>>>((const float*)x, Wg, bias, logits, T, d, E);
     }
     return hipGetLastError();
 }

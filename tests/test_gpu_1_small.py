@@ -56,7 +56,7 @@ def test_edge_shapes(wl):
     (256, 64, BF16), (257, 64, BF16),      # few-token router: 8- then 16-token blocks
     (512, 40, F32), (513, 40, F32),        # ... then the MFMA kernel (E not a multiple of 64)
     (513, 64, BF16), (2500, 257, BF16),    # ragged 64-token and 64-expert tails
-    (8192, 64, BF16), (8193, 72, BF16),    # many tokens, one token past a block
+    (8192, 64, BF16), (8193, 72, BF16),    # many tokens, one token past a block; both MFMA stage-loop forms
     (600, 1024, BF16), (700, 1, F32),      # the largest E, and a single expert, on the matrix cores
 ], ids=lambda v: str(v))
 def test_router_kernel_boundaries(T, E, act):
