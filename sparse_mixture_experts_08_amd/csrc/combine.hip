@@ -13,7 +13,7 @@ namespace moe {
 // K > 0: k fixed at compile time, so the slot sort is a register-only network and the k + 1 row loads of a
 // vector are all in flight together; K = 0: any k <= 16, one row load at a time.
 template <bool ACT_BF16, int K>
-__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ pos, const float* __restrict__ w,
+__global__ __launch_bounds__(512) void combine_kernel(const int32_t* __restrict__ pos, const float* __restrict__ w,
                                                       const uint8_t* __restrict__ y_rows, int T, int d, int k_rt,
                                                       uint8_t* __restrict__ y)
 {
@@ -120,13 +120,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
 }
 
-static constexpr int COMBINE_THREADS = 256;
-
-// Grid: with few tokens one block per (token, column chunk), so decode-sized T still spreads over the
-// CUs; with many tokens one block per token, which amortises the slot sort over the row.  256-thread
-// blocks step a 7168-wide bf16 row in three and a half 16-byte vectors per thread, a little faster than
-// 128-thread blocks in seven (32768-token fp8 layer 0.939 -> 0.917 ms, 16384-token skewed 0.469 ->
-// 0.451 ms; 64 threads 0.953 / 0.477).
+// Threads per block.  Grid: with few tokens one block per (token, column chunk) of 256-thread blocks, so
+// decode-sized T still spreads over the CUs; with many tokens one block per token, which amortises the slot
+// sort over the row, of 448 threads, which step a 7168-wide bf16 row in exactly two 16-byte vectors each
+// (32768-token fp8 layer 0.908 -> 0.879 ms against 256 threads' three and a half, 16384-token skewed 0.446
+// -> 0.431 ms; 512 threads 0.881 / 0.433, 224 0.909 / 0.444; 128 and 64 threads slower still, 0.917 /
+// 0.451 and 0.953 / 0.477 against 256 threads at 0.939 / 0.469 in an earlier run).
+static int combine_threads(const moe_shape_t& s) { return s.T >= 1024 ? 448 : 256; }
 static dim3 combine_grid(const moe_shape_t& s, int threads)
 {
     const int ve = s.act_dtype == MOE_BF16 ? 8 : 4;
@@ -138,15 +138,16 @@ template <bool ACT_BF16>
 static void launch_combine_t(const moe_shape_t& s, const int32_t* pos, const float* w, const Workspace& ws, void* y,
                              hipStream_t stream)
 {
-    const dim3 grid = combine_grid(s, COMBINE_THREADS);
+    const int nt = combine_threads(s);
+    const dim3 grid = combine_grid(s, nt);
     const int T = (int)s.T, d = (int)s.d, k = (int)s.k;
     const uint8_t* rows = (const uint8_t*)ws.y_rows;
     uint8_t* out = (uint8_t*)y;
     switch (k) {
-    case 4: combine_kernel<ACT_BF16, 4><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
-    case 6: combine_kernel<ACT_BF16, 6><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
-    case 8: combine_kernel<ACT_BF16, 8><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
-    default: combine_kernel<ACT_BF16, 0><<<grid, COMBINE_THREADS, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 4: combine_kernel<ACT_BF16, 4><<<grid, nt, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 6: combine_kernel<ACT_BF16, 6><<<grid, nt, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    case 8: combine_kernel<ACT_BF16, 8><<<grid, nt, 0, stream>>>(pos, w, rows, T, d, k, out); break;
+    default: combine_kernel<ACT_BF16, 0><<<grid, nt, 0, stream>>>(pos, w, rows, T, d, k, out); break;
     }
 }
 
